@@ -1,0 +1,19 @@
+"""float64 CPU oracle for paged KV-cache attention -- test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this package.
+"""
+from .paged_oracle import (  # noqa: F401
+    ESIZE,
+    PageLayout,
+    row_offset,
+    pool_row_offset,
+    place,
+    gather,
+    read_pooled,
+    decode,
+    prefill,
+    sparse,
+    pool,
+    scores,
+    topk,
+)

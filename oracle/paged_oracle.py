@@ -1,0 +1,336 @@
+"""Plain float64 CPU oracle for attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library (its own row
+addressing, its own arena layout, its own arithmetic) and is deliberately slow
+and obvious.
+
+Sources (page titles and sections; the pages print no source code and no
+numeric worked example for these kernels):
+  [P1] TensorFold PR #1169, "Flash Next attention caches readable through a
+       page table" -- sections "What this changes" and "Receipt".
+  [P2] TensorFold PR #1170, "Flash Next CUDA: the streams beside the first take
+       KV pages from the core pool" -- description and commit messages 3f5b87d
+       (Seg / kv_row), ce5b78d (attention partials) and 85aeb4b (Pg / pg_at).
+
+Readings taken where the pages are silent are listed in the design doc (the
+"readings" table); each function below names the ones it relies on.
+
+Parity status per function:
+  page_layout / row_offset / place / gather : pinned (hand-derived offsets,
+      round trip, red controls)
+  decode / prefill / sparse                 : pinned (closed forms, invariants,
+      50-digit brute force on tiny shapes)
+  pool                                      : pinned (closed forms, exact quarters)
+  scores                                    : pinned (exact integer scores,
+      one-hot rows, linearity)
+  topk                                      : pinned (brute-force sort, ties)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+ESIZE = {"bf16": 2, "f32": 4}
+
+
+# ---------------------------------------------------------------------------
+# Row addressing and the page layout
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PageLayout:
+    """Where each region of one attention layer sits inside a page.
+
+    [P1 "What this changes"]: a page of n positions holds, for each attention
+    layer, the keys, values and indexer keys of its n positions and the pooled
+    rows of their n/4 blocks.  [P2 commit 3f5b87d]: inside a page the order is
+    [key, value][head][position][row].  Reading (S1): K [Hkv][n][D], then
+    V [Hkv][n][D], then IK [n][DI], then POOL [n/4][DI] float32.
+    All offsets are in bytes.
+    """
+    n_kv_heads: int
+    head_dim: int
+    page_pos: int
+    dtype: str
+    idx_dim: int = 0
+
+    @property
+    def esize(self) -> int:
+        return ESIZE[self.dtype]
+
+    @property
+    def k_off(self) -> int:
+        return 0
+
+    @property
+    def v_off(self) -> int:
+        return self.n_kv_heads * self.page_pos * self.head_dim * self.esize
+
+    @property
+    def ik_off(self) -> int:
+        return 2 * self.v_off
+
+    @property
+    def pool_off(self) -> int:
+        return self.ik_off + self.page_pos * self.idx_dim * self.esize
+
+    @property
+    def page_bytes(self) -> int:
+        if self.idx_dim == 0:
+            return self.ik_off
+        return self.pool_off + (self.page_pos // 4) * self.idx_dim * 4
+
+    @property
+    def page_elems(self) -> int:
+        """Elements of the arena type in one page (the pages' "elements in a page")."""
+        assert self.page_bytes % self.esize == 0
+        return self.page_bytes // self.esize
+
+
+def row_offset(table, page_pos: int, page_elems: int, s: int, h: int, p: int, width: int,
+               rows_per_head: Optional[int] = None) -> int:
+    """Element offset of row (stream s, head h, position p) in a region whose page part is
+    [H][rows_per_head][width].
+
+    [P1 "What this changes"]: with no table the old contiguous expression; with a
+    table the start of the page that holds the position plus the row inside that
+    page.  [P2 commit 3f5b87d]: with no table a stream keeps "cap rows a head",
+    which is this same expression with page_pos = cap and the implicit table [s].
+    """
+    if rows_per_head is None:
+        rows_per_head = page_pos
+    if table is None:
+        page = s
+        within = p
+    else:
+        page = int(table[s][p // page_pos])
+        within = p % page_pos
+    return page * page_elems + (h * rows_per_head + within) * width
+
+
+def pool_row_offset(table, page_pos: int, page_elems_f32: int, s: int, b: int, width: int) -> int:
+    """Float32-element offset of the pooled row of block b (positions 4b..4b+3).
+
+    The block's rows share one page because page_pos is a multiple of 4
+    ([P2 "What this changes"]: n must be a multiple of 4); its pooled row is
+    row (4b mod n)/4 of that page's POOL region.
+    """
+    p = 4 * b
+    if table is None:
+        page, within = s, p
+    else:
+        page, within = int(table[s][p // page_pos]), p % page_pos
+    return page * page_elems_f32 + (within // 4) * width
+
+
+def place(layout: PageLayout, table, n_pages: int, lens: Sequence[int], K, V, IK=None) -> np.ndarray:
+    """Write each stream's rows into a fresh arena (bytes) through the table.
+
+    K, V: [S][Hkv][cap][D] element arrays (uint16 bf16 bits or float32).
+    IK:   [S][cap][DI] or None.  Rows past lens[s] are not written.
+    The arena starts zero-filled.
+    """
+    arena = np.zeros(n_pages * layout.page_bytes, dtype=np.uint8)
+    es = layout.esize
+    D = layout.head_dim
+    pe = layout.page_elems
+    kview = arena.view(np.uint16 if es == 2 else np.float32)
+    for s, L in enumerate(lens):
+        # a logical page's rows are consecutive inside its arena page, so copy a page part at once
+        for p0 in range(0, L, layout.page_pos):
+            n = min(layout.page_pos, L - p0)
+            for h in range(layout.n_kv_heads):
+                ko = row_offset(table, layout.page_pos, pe, s, h, p0, D) + layout.k_off // es
+                vo = row_offset(table, layout.page_pos, pe, s, h, p0, D) + layout.v_off // es
+                kview[ko:ko + n * D] = np.asarray(K[s, h, p0:p0 + n]).reshape(-1)
+                kview[vo:vo + n * D] = np.asarray(V[s, h, p0:p0 + n]).reshape(-1)
+            if IK is not None and layout.idx_dim:
+                DI = layout.idx_dim
+                io = row_offset(table, layout.page_pos, pe, s, 0, p0, DI) + layout.ik_off // es
+                kview[io:io + n * DI] = np.asarray(IK[s, p0:p0 + n]).reshape(-1)
+    return arena
+
+
+def gather(layout: PageLayout, table, arena: np.ndarray, lens: Sequence[int], cap: Optional[int] = None):
+    """Inverse of place(): read K, V (and IK when the layout has it) back into logical form,
+    one row at a time through row_offset()."""
+    es = layout.esize
+    D = layout.head_dim
+    pe = layout.page_elems
+    view = arena.view(np.uint16 if es == 2 else np.float32)
+    cap = int(cap if cap is not None else max(list(lens) + [1]))
+    S = len(lens)
+    K = np.zeros((S, layout.n_kv_heads, cap, D), dtype=view.dtype)
+    V = np.zeros_like(K)
+    IK = np.zeros((S, cap, layout.idx_dim), dtype=view.dtype) if layout.idx_dim else None
+    for s, L in enumerate(lens):
+        for h in range(layout.n_kv_heads):
+            for p in range(L):
+                o = row_offset(table, layout.page_pos, pe, s, h, p, D)
+                K[s, h, p] = view[o + layout.k_off // es: o + layout.k_off // es + D]
+                V[s, h, p] = view[o + layout.v_off // es: o + layout.v_off // es + D]
+        if IK is not None:
+            DI = layout.idx_dim
+            for p in range(L):
+                o = row_offset(table, layout.page_pos, pe, s, 0, p, DI) + layout.ik_off // es
+                IK[s, p] = view[o:o + DI]
+    return K, V, IK
+
+
+def read_pooled(layout: PageLayout, table, arena: np.ndarray, s: int, n_blocks: int) -> np.ndarray:
+    """Read the float32 pooled rows of blocks 0..n_blocks-1 of stream s from the arena."""
+    f32 = arena.view(np.float32)
+    pe32 = layout.page_bytes // 4
+    DI = layout.idx_dim
+    out = np.zeros((n_blocks, DI), dtype=np.float32)
+    for b in range(n_blocks):
+        o = pool_row_offset(table, layout.page_pos, pe32, s, b, DI) + layout.pool_off // 4
+        out[b] = f32[o:o + DI]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Attention (decode, prefill, sparse)
+# ---------------------------------------------------------------------------
+
+def _softmax_rows_attend(z: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Textbook softmax attention in float64: w = exp(z - max z); out = (w V) / sum w."""
+    m = np.max(z, axis=-1, keepdims=True)
+    w = np.exp(z - m)
+    return (w @ V) / np.sum(w, axis=-1, keepdims=True)
+
+
+def decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, lens: Sequence[int], scale: float) -> np.ndarray:
+    """Dense decode attention, float64.
+
+    q [S][Hq][D], K/V [S][Hkv][cap][D] (exact input values as float64).
+    Query head h reads KV head h // (Hq/Hkv) (reading S14) over all cached
+    positions 0..L-1 (reading S12).  A stream with L = 0 gives a zero row (S22).
+    [P1 "What this changes"]: fn_attn_chunks produces the dense attention rows.
+    """
+    S, Hq, D = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for s in range(S):
+        L = int(lens[s])
+        if L == 0:
+            continue
+        for h in range(Hq):
+            g = h // G
+            z = scale * (K[s, g, :L] @ q[s, h])
+            out[s, h] = _softmax_rows_attend(z[None, :], V[s, g, :L])[0]
+    return out
+
+
+def prefill(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos0: int, scale: float, causal: bool = True,
+            rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Causal prompt attention for one chunk of queries, float64.
+
+    q [Nq][Hq][D] are the queries at absolute positions q_pos0 .. q_pos0+Nq-1;
+    K/V [Hkv][cap][D] hold positions 0 .. q_pos0+Nq-1 (stored before the chunk).
+    Query at position p attends to keys j <= p (reading S13); without the mask
+    to every key 0 .. q_pos0+Nq-1.  ``rows`` limits the work to some query rows
+    (the result still has Nq rows; others are zero).
+    """
+    Nq, Hq, D = q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    Lk = q_pos0 + Nq
+    out = np.zeros((Nq, Hq, D), dtype=np.float64)
+    sel = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    if len(sel) == 0:
+        return out
+    for h in range(Hq):
+        g = h // G
+        Kg = K[g, :Lk]
+        Vg = V[g, :Lk]
+        z = scale * (q[sel, h] @ Kg.T)            # [n][Lk]
+        if causal:
+            pos = q_pos0 + sel
+            mask = np.arange(Lk)[None, :] > pos[:, None]
+            z = np.where(mask, -np.inf, z)
+        out[sel, h] = _softmax_rows_attend(z, Vg)
+    return out
+
+
+def sparse(q: np.ndarray, K: np.ndarray, V: np.ndarray, block_ids: Sequence[Sequence[int]], scale: float) -> np.ndarray:
+    """Attention over the selected blocks only, float64.
+
+    Block b covers positions 4b .. 4b+3 ([P1 "What this changes"]: pooled rows
+    of blocks of four).  The rows attended are those positions of the selected
+    blocks (reading S11: ascending); with no selected block the row is zero.
+    """
+    S, Hq, D = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for s in range(S):
+        ids = sorted(int(b) for b in block_ids[s])
+        if not ids:
+            continue
+        pos = np.array([4 * b + j for b in ids for j in range(4)], dtype=np.int64)
+        for h in range(Hq):
+            g = h // G
+            z = scale * (K[s, g, pos] @ q[s, h])
+            out[s, h] = _softmax_rows_attend(z[None, :], V[s, g, pos])[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Block pooling, block scores, top-k
+# ---------------------------------------------------------------------------
+
+def pool(IK: np.ndarray, lens: Sequence[int]) -> list:
+    """Mean of the indexer-key rows of each complete block of four positions.
+
+    IK [S][cap][DI] exact values as float64.  For b < floor(L/4):
+    pooled[b] = float32(((IK[4b] + IK[4b+1]) + IK[4b+2]) + IK[4b+3]) / 4)
+    with the sum in float64 (exact for bf16 rows whose exponents lie within 43
+    binades), one rounding to float32 (readings S3, S4, S5).
+    [P1 "What this changes"]: the pool kernel reads once per block of four and
+    the page holds the pooled rows of its n/4 blocks.
+    Returns a list of [nb_s][DI] float32 arrays.
+    """
+    out = []
+    for s, L in enumerate(lens):
+        nb = int(L) // 4
+        x = IK[s, :4 * nb].reshape(nb, 4, IK.shape[-1])
+        acc = ((x[:, 0] + x[:, 1]) + x[:, 2]) + x[:, 3]
+        out.append((acc * 0.25).astype(np.float32))
+    return out
+
+
+def scores(qI: np.ndarray, pooled: np.ndarray) -> np.ndarray:
+    """Block scores: sum over indexer heads of the dot product of the head's
+    indexer query with the block's pooled row, in float64.
+
+    qI [Hi][DI] exact values (float64), pooled [nb][DI] float32.
+    Accumulation order (reading S7): one float64 accumulator per block, terms
+    added head by head and, within a head, dimension by dimension.  Every
+    product of a bf16 query and a float32 pooled value is exact in float64, so
+    the only roundings are those of the additions, in this order.
+    """
+    P = pooled.astype(np.float64)
+    acc = np.zeros(P.shape[0], dtype=np.float64)
+    Hi, DI = qI.shape
+    for h in range(Hi):
+        for d in range(DI):
+            acc = acc + qI[h, d] * P[:, d]
+    return acc
+
+
+def topk(score: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the k highest scores, lowest id first among equal scores, returned ascending.
+
+    Orders by (score descending, id ascending); -0.0 equals +0.0; when there are
+    no more than k blocks every block is selected (readings S8, S9, S10).
+    """
+    nb = score.shape[0]
+    ids = np.arange(nb)
+    order = np.lexsort((ids, -score))
+    return np.sort(order[:min(k, nb)])

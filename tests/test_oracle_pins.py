@@ -1,0 +1,347 @@
+"""Pins of the float64 oracle against facts fixed by the pages and by mathematics.
+
+Each test names the passage whose definition it checks.  The oracle is never
+compared with itself: expectations come from hand-derived offsets, closed
+forms, invariants, exact integer arithmetic, Python's own sort, or 50-digit
+mpmath evaluation on tiny shapes.  Each pin is chosen so that a plausible slip
+in the oracle (a dropped scale, a GQA map taken modulo instead of divided, an
+off-by-one length or causal mask, a wrong block offset, a reversed tie rule,
+transposed operands) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from paged_kv_cache_pg_amd.inputs import make_workload, make_table, bf16_bits_to_f32, f32_to_bf16_bits
+
+
+# ----------------------------------------------------------------------------
+# Row addressing ("What this changes", PR #1169; commit 3f5b87d, PR #1170)
+# ----------------------------------------------------------------------------
+
+def test_row_offset_hand_derived():
+    # table row for stream 0: logical page 0 -> arena page 2, page 1 -> 0, page 2 -> 1
+    table = [[2, 0, 1], [1, 1, 1]]
+    ptok, pe, W = 4, 100, 8
+    # position 5 sits in logical page 1 (arena page 0), row 1 of head 1 inside it: (1*4 + 1) * 8
+    assert O.row_offset(table, ptok, pe, 0, 1, 5, W) == 40
+    # position 9: logical page 2 -> arena page 1 (start 100), row 1 of head 0
+    assert O.row_offset(table, ptok, pe, 0, 0, 9, W) == 108
+    # position 0 of head 0: start of arena page 2
+    assert O.row_offset(table, ptok, pe, 0, 0, 0, W) == 200
+    # position 3 of head 1 in stream 1: arena page 1, row (4 + 3)
+    assert O.row_offset(table, ptok, pe, 1, 1, 3, W) == 100 + 7 * 8
+    # no table: cap rows a head, stream s at s * pe (cap = 12 here)
+    assert O.row_offset(None, 12, 1000, 1, 1, 5, W) == 1000 + (12 + 5) * 8
+    assert O.row_offset(None, 12, 1000, 0, 0, 11, W) == 11 * 8
+
+
+def test_pool_row_offset_hand_derived():
+    table = [[3, 1]]
+    # block 5 = positions 20..23; page_pos 16 -> logical page 1 -> arena page 1; row (20 % 16)/4 = 1
+    assert O.pool_row_offset(table, 16, 50, 0, 5, 128) == 50 + 128
+    # block 0 -> arena page 3, row 0
+    assert O.pool_row_offset(table, 16, 50, 0, 0, 128) == 150
+
+
+def test_layout_sizes():
+    # a 256-position page of 4 KV heads x 256 dims in bf16: K and V only
+    L = O.PageLayout(4, 256, 256, "bf16")
+    assert L.page_elems == 2 * 4 * 256 * 256 == 524288
+    # with indexer keys (128 wide) and pooled rows (float32, 64 of them)
+    L = O.PageLayout(4, 256, 256, "bf16", idx_dim=128)
+    assert L.page_bytes == 2 * 524288 + 256 * 128 * 2 + 64 * 128 * 4 == 1146880
+    L = O.PageLayout(2, 256, 16, "f32")
+    assert L.page_elems == 16384
+
+
+@pytest.mark.parametrize("kind", ["reversed", "shuffled", "identity"])
+@pytest.mark.parametrize("ptok", [4, 12, 16])
+def test_place_gather_round_trip(kind, ptok):
+    w = make_workload(7, [37, 5, 16], ptok, 4, 2, head_dim=8, dtype="bf16", table_kind=kind, idx_dim=4, n_idx_heads=1)
+    lay = O.PageLayout(2, 8, ptok, "bf16", idx_dim=4)
+    arena = O.place(lay, w.table, w.n_pages, w.lens, w.K, w.V, w.IK)
+    K, V, IK = O.gather(lay, w.table, arena, w.lens)
+    for s, L in enumerate(w.lens):
+        assert np.array_equal(K[s, :, :L], w.K[s, :, :L])
+        assert np.array_equal(V[s, :, :L], w.V[s, :, :L])
+        assert np.array_equal(IK[s, :L], w.IK[s, :L])
+
+
+def test_paged_equals_contiguous_arena_bytes():
+    """Only addresses change: the rows read back are the same bytes either way."""
+    w = make_workload(3, [50, 33], 8, 4, 2, head_dim=8, dtype="bf16", table_kind="shuffled")
+    lay_p = O.PageLayout(2, 8, 8, "bf16")
+    lay_c = O.PageLayout(2, 8, 50, "bf16")  # contiguous: page_pos = cap
+    ap = O.place(lay_p, w.table, w.n_pages, w.lens, w.K, w.V)
+    ac = O.place(lay_c, None, 2, w.lens, w.K, w.V)
+    Kp, Vp, _ = O.gather(lay_p, w.table, ap, w.lens, cap=50)
+    Kc, Vc, _ = O.gather(lay_c, None, ac, w.lens, cap=50)
+    assert np.array_equal(Kp, Kc) and np.array_equal(Vp, Vc)
+
+
+def test_red_controls_swapped_table_and_planted_row():
+    """PR #1169 "Receipt": a swapped table over placed pages and a planted row must both fail."""
+    w = make_workload(11, [40, 24], 8, 4, 2, head_dim=8, dtype="f32", table_kind="shuffled")
+    lay = O.PageLayout(2, 8, 8, "f32")
+    arena = O.place(lay, w.table, w.n_pages, w.lens, w.K, w.V)
+    q = w.as_f64("q")
+    K0, V0, _ = O.gather(lay, w.table, arena, w.lens)
+    ref = O.decode(q, K0.astype(np.float64), V0.astype(np.float64), w.lens, 0.25)
+    # swap two placed pages across the streams' table rows
+    t2 = w.table.copy()
+    t2[0, 1], t2[1, 0] = w.table[1, 0], w.table[0, 1]
+    K1, V1, _ = O.gather(lay, t2, arena, w.lens)
+    got = O.decode(q, K1.astype(np.float64), V1.astype(np.float64), w.lens, 0.25)
+    assert not np.array_equal(got, ref)
+    # plant a row: overwrite one value row of stream 1 inside the arena
+    a2 = arena.copy()
+    off = O.row_offset(w.table, 8, lay.page_elems, 1, 1, 13, 8) + lay.v_off // 4
+    a2.view(np.float32)[off:off + 8] += 1.0
+    K2, V2, _ = O.gather(lay, w.table, a2, w.lens)
+    got2 = O.decode(q, K2.astype(np.float64), V2.astype(np.float64), w.lens, 0.25)
+    assert not np.array_equal(got2[1], ref[1]) and np.array_equal(got2[0], ref[0])
+
+
+# ----------------------------------------------------------------------------
+# Dense decode attention ("What this changes"/"Receipt", PR #1169)
+# ----------------------------------------------------------------------------
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_decode_single_key_is_value_row():
+    q, K, V = _rand((1, 4, 16), 1), _rand((1, 2, 5, 16), 2), _rand((1, 2, 5, 16), 3)
+    out = O.decode(q, K, V, [1], 1 / 4)
+    for h in range(4):
+        assert np.array_equal(out[0, h], V[0, h // 2, 0])
+
+
+def test_decode_zero_query_is_mean_of_values_over_exactly_L_rows():
+    L = 9
+    q = np.zeros((1, 2, 8))
+    K, V = _rand((1, 1, 12, 8), 4), _rand((1, 1, 12, 8), 5)
+    out = O.decode(q, K, V, [L], 0.5)
+    assert np.allclose(out[0, 0], V[0, 0, :L].mean(axis=0), rtol=0, atol=1e-14)
+    # values equal to the position index: the mean over 0..L-1 is (L-1)/2, not L/2
+    Vp = np.broadcast_to(np.arange(12.0)[None, None, :, None], (1, 1, 12, 8)).copy()
+    out = O.decode(q, K, Vp, [L], 0.5)
+    assert np.allclose(out, (L - 1) / 2, rtol=0, atol=1e-13)
+
+
+def test_decode_two_keys_logistic_closed_form():
+    # scores a*scale and b*scale; weight of key 1 is the logistic function of their difference
+    D = 4
+    q = np.array([[[1.0, 2.0, 0.0, -1.0]]])
+    k0 = np.array([0.5, 0.0, 1.0, 0.0])    # q.k0 = 0.5
+    k1 = np.array([1.0, 1.0, 0.0, 1.0])    # q.k1 = 2.0
+    K = np.stack([k0, k1])[None, None]
+    V = np.array([[1.0, 0, 0, 0], [0, 3.0, 0, 0]])[None, None]
+    scale = 0.7
+    out = O.decode(q, K, V, [2], scale)[0, 0]
+    w1 = 1.0 / (1.0 + math.exp(scale * (0.5 - 2.0)))
+    assert abs(out[0] - (1 - w1)) < 1e-15 and abs(out[1] - 3 * w1) < 1e-15
+    # scale enters once: doubling it is the same as doubling q
+    assert np.allclose(O.decode(q, K, V, [2], 2 * scale), O.decode(2 * q, K, V, [2], scale), atol=1e-15)
+
+
+def test_decode_gqa_head_map_is_division():
+    # query head h reads KV head h // G; KV head g holds values g + 1 everywhere
+    Hq, Hkv, D, L = 8, 2, 4, 6
+    q, K = _rand((1, Hq, D), 6), _rand((1, Hkv, L, D), 7)
+    V = np.zeros((1, Hkv, L, D))
+    for g in range(Hkv):
+        V[0, g] = g + 1
+    out = O.decode(q, K, V, [L], 0.5)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], h // (Hq // Hkv) + 1, atol=1e-14)
+
+
+def test_decode_dominant_key_and_affine_equivariance():
+    D, L = 16, 7
+    K = _rand((1, 1, L, D), 8)
+    V = _rand((1, 1, L, D), 9)
+    q = 64.0 * K[:, :, 3]                       # q aligned with key 3, huge margin
+    out = O.decode(q, K, V, [L], 1.0)
+    assert np.allclose(out[0, 0], V[0, 0, 3], atol=1e-12)
+    q2 = _rand((1, 1, D), 10)
+    a, c = -1.5, 0.25
+    o1 = O.decode(q2, K, V, [L], 0.3)
+    o2 = O.decode(q2, K, a * V + c, [L], 0.3)
+    assert np.allclose(o2, a * o1 + c, atol=1e-13)
+
+
+@pytest.mark.parametrize("D,L,G", [(4, 1, 1), (4, 5, 2), (8, 12, 4), (8, 7, 1)])
+def test_decode_matches_50_digit_brute_force(D, L, G):
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    Hkv = 2
+    Hq = Hkv * G
+    q, K, V = _rand((1, Hq, D), 20 + L), _rand((1, Hkv, L, D), 30 + L), _rand((1, Hkv, L, D), 40 + L)
+    scale = 1 / math.sqrt(D)
+    out = O.decode(q, K, V, [L], scale)
+    for h in range(Hq):
+        g = h // G
+        z = [mp.mpf(scale) * mp.fsum(mp.mpf(q[0, h, d]) * mp.mpf(K[0, g, j, d]) for d in range(D)) for j in range(L)]
+        e = [mp.exp(x) for x in z]
+        tot = mp.fsum(e)
+        for d in range(D):
+            ref = mp.fsum(e[j] * mp.mpf(V[0, g, j, d]) for j in range(L)) / tot
+            assert abs(float(ref) - out[0, h, d]) <= 1e-13 * max(1.0, abs(float(ref)))
+
+
+def test_decode_empty_stream_is_zero():
+    out = O.decode(_rand((2, 2, 4), 1), _rand((2, 1, 3, 4), 2), _rand((2, 1, 3, 4), 3), [0, 3], 0.5)
+    assert np.array_equal(out[0], np.zeros((2, 4)))
+
+
+# ----------------------------------------------------------------------------
+# Prefill (causal prompt attention over the paged cache; PR #1170 maintainer reply)
+# ----------------------------------------------------------------------------
+
+def test_prefill_first_row_and_causal_mask_offsets():
+    Hq, Hkv, D, N = 4, 2, 8, 10
+    q, K, V = _rand((N, Hq, D), 50), _rand((Hkv, N, D), 51), _rand((Hkv, N, D), 52)
+    out = O.prefill(q, K, V, 0, 0.3, causal=True)
+    for h in range(Hq):
+        assert np.array_equal(out[0, h], V[h // 2, 0])            # position 0 sees only key 0
+    # equal keys and value = position: causal row p is the mean of 0..p = p/2
+    Ke = np.ones((Hkv, N, D))
+    Vp = np.broadcast_to(np.arange(N, dtype=np.float64)[None, :, None], (Hkv, N, D)).copy()
+    out = O.prefill(q, Ke, Vp, 0, 0.3, causal=True)
+    for p in range(N):
+        assert np.allclose(out[p], p / 2, atol=1e-13)
+    # without the mask every row sees all N keys
+    out = O.prefill(q, Ke, Vp, 0, 0.3, causal=False)
+    assert np.allclose(out, (N - 1) / 2, atol=1e-13)
+
+
+def test_prefill_rows_equal_decode_and_chunking_invariance():
+    Hq, Hkv, D, N = 4, 1, 8, 24
+    q, K, V = _rand((N, Hq, D), 60), _rand((Hkv, N, D), 61), _rand((Hkv, N, D), 62)
+    full = O.prefill(q, K, V, 0, 0.4)
+    # a row at position p equals decode over p+1 cached rows
+    for p in (0, 5, 23):
+        dec = O.decode(q[p][None], K[None], V[None], [p + 1], 0.4)[0]
+        assert np.allclose(full[p], dec, atol=1e-14)
+    # chunks of 8 queries against the growing cache give the same rows
+    parts = [O.prefill(q[c:c + 8], K, V, c, 0.4) for c in range(0, N, 8)]
+    assert np.allclose(np.concatenate(parts), full, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Block pooling ("What this changes", PR #1169: pooled rows of n/4 blocks)
+# ----------------------------------------------------------------------------
+
+def test_pool_closed_forms():
+    L, DI = 19, 6
+    # rows equal to their position: block b pools 4b..4b+3 -> 4b + 1.5; 19 rows -> 4 complete blocks
+    IK = np.broadcast_to(np.arange(L, dtype=np.float64)[:, None], (L, DI))[None].copy()
+    (p,) = O.pool(IK, [L])
+    assert p.shape == (4, DI) and p.dtype == np.float32
+    for b in range(4):
+        assert np.all(p[b] == 4 * b + 1.5)
+    # four equal rows pool to that row (bf16 values, exact)
+    x = bf16_bits_to_f32(f32_to_bf16_bits(_rand((DI,), 70).astype(np.float32))).astype(np.float64)
+    (p,) = O.pool(np.tile(x, (1, 4, 1)), [4])
+    assert np.array_equal(p[0], x.astype(np.float32))
+    # 1, 2, 3, 4 -> 2.5 exactly; mixed magnitudes stay exact (sum in float64)
+    IK = np.array([[[1.0], [2.0], [3.0], [4.0]]])
+    assert O.pool(IK, [4])[0][0, 0] == 2.5
+    IK = np.array([[[2.0 ** 20], [2.0 ** -20], [-(2.0 ** 20)], [2.0 ** -21]]])
+    assert O.pool(IK, [4])[0][0, 0] == np.float32((2.0 ** -20 + 2.0 ** -21) / 4)
+
+
+def test_pool_of_short_stream_is_empty():
+    assert O.pool(np.zeros((1, 3, 4)), [3])[0].shape == (0, 4)
+
+
+# ----------------------------------------------------------------------------
+# Block scores and top-k (QSA scoring; sparse selection)
+# ----------------------------------------------------------------------------
+
+def test_scores_exact_on_integers_and_linear_in_heads():
+    rng = np.random.default_rng(80)
+    Hi, DI, nb = 4, 16, 50
+    qI = rng.integers(-3, 4, size=(Hi, DI)).astype(np.float64)
+    pooled = rng.integers(-5, 6, size=(nb, DI)).astype(np.float32)
+    got = O.scores(qI, pooled)
+    for b in range(nb):
+        exact = sum(int(qI[h, d]) * int(pooled[b, d]) for h in range(Hi) for d in range(DI))
+        assert got[b] == exact
+    # a one-hot query in one head picks one pooled column
+    e = np.zeros((Hi, DI))
+    e[2, 5] = 1.0
+    assert np.array_equal(O.scores(e, pooled), pooled[:, 5].astype(np.float64))
+    # a head-summed query gives the same score when everything is exact
+    qs = np.zeros((Hi, DI))
+    qs[0] = qI.sum(axis=0)
+    assert np.array_equal(O.scores(qs, pooled), got)
+
+
+def test_topk_matches_python_sort_and_ties():
+    rng = np.random.default_rng(81)
+    for trial in range(20):
+        nb = int(rng.integers(1, 60))
+        sc = rng.integers(-2, 3, size=nb).astype(np.float64)   # many exact ties
+        k = int(rng.integers(1, 70))
+        want = sorted(sorted(range(nb), key=lambda b: (-sc[b], b))[:k])
+        assert list(O.topk(sc, k)) == want
+    assert list(O.topk(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 2)) == [1, 2]
+    assert list(O.topk(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 4)) == [1, 2, 3, 4]
+    assert list(O.topk(np.full(10, 0.5), 3)) == [0, 1, 2]
+    assert list(O.topk(np.array([5.0, 1.0]), 9)) == [0, 1]
+    # -0.0 equals +0.0: the lower id wins
+    assert list(O.topk(np.array([-1.0, 0.0, -0.0, -2.0]), 1)) == [1]
+    assert list(O.topk(np.array([-1.0, -0.0, 0.0, -2.0]), 1)) == [1]
+
+
+# ----------------------------------------------------------------------------
+# Sparse attention over the selected blocks
+# ----------------------------------------------------------------------------
+
+def test_sparse_all_blocks_is_dense_and_subset_is_row_restriction():
+    S, Hq, Hkv, D, L = 2, 4, 2, 8, 16
+    q, K, V = _rand((S, Hq, D), 90), _rand((S, Hkv, L, D), 91), _rand((S, Hkv, L, D), 92)
+    dense = O.decode(q, K, V, [L, L], 0.3)
+    allb = O.sparse(q, K, V, [list(range(4)), list(range(4))], 0.3)
+    assert np.allclose(allb, dense, atol=1e-15)
+    sel = [[3, 1], [0]]
+    got = O.sparse(q, K, V, sel, 0.3)
+    for s in range(S):
+        pos = [4 * b + j for b in sorted(sel[s]) for j in range(4)]
+        want = O.decode(q[s:s + 1], K[s:s + 1][:, :, pos], V[s:s + 1][:, :, pos], [len(pos)], 0.3)
+        assert np.allclose(got[s], want[0], atol=1e-15)
+    assert np.array_equal(O.sparse(q, K, V, [[], [0]], 0.3)[0], np.zeros((Hq, D)))
+
+
+def test_make_table_shapes():
+    t, n = make_table("reversed", [3])
+    assert n == 3 and list(t[0]) == [2, 1, 0]
+    t, n = make_table("shuffled", [2, 3], np.random.default_rng(0))
+    assert n == 5 and sorted(list(t[0, :2]) + list(t[1, :3])) == [0, 1, 2, 3, 4]
+
+
+def test_oracle_matches_its_stored_small_case():
+    """tests/golden/oracle_small.json was written by tests/golden/make_golden.py (oracle only)."""
+    import json
+    import os
+    import sys
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    sys.path.insert(0, here)
+    try:
+        import make_golden
+    finally:
+        sys.path.remove(here)
+    with open(os.path.join(here, "oracle_small.json")) as f:
+        stored = json.load(f)
+    now = make_golden.compute()
+    for key in ("decode", "pooled", "scores", "topk2", "sparse", "prefill_q0x3_at10"):
+        a, b = now[key], stored[key]
+        if key in ("pooled", "scores", "topk2"):
+            assert all(np.array_equal(np.array(x), np.array(y)) for x, y in zip(a, b)), key
+        else:
+            assert np.allclose(np.array(a), np.array(b), rtol=0, atol=1e-14), key
