@@ -1,0 +1,241 @@
+/*
+ * paged_attn.h -- C ABI of libpagedattn.so: attention over a KV cache read
+ * through an int page table, on one AMD MI355X (gfx950).
+ *
+ * Sources (page titles and sections):
+ *   [P1] TensorFold PR #1169 "Flash Next attention caches readable through a
+ *        page table", sections "What this changes" and "Receipt".
+ *   [P2] TensorFold PR #1170 "Flash Next CUDA: the streams beside the first
+ *        take KV pages from the core pool": description, commit messages
+ *        3f5b87d (Seg/kv_row), ce5b78d (attention partials branch once),
+ *        1ac2075 (pool runs), 51f8354 (mapRun refuses a short run) and the
+ *        maintainer replies (drain before free; page-run prompt path).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Page table (the pages' Pg argument, [P1 "What this changes"]): an int page
+ * table, the elements in a page and the positions in a page.  The row of
+ * (stream s, head h, position p) in a region whose page part is
+ * [H][page_pos][W] starts at element
+ *     table[s * table_stride + p / page_pos] * page_elems + (h * page_pos + p % page_pos) * W
+ * and, with no table (table == NULL), at the old contiguous expression
+ *     s * page_elems + (h * cap + p) * W       with page_pos = cap,
+ * i.e. each stream keeps "cap rows a head" ([P2 commit 3f5b87d]).  page_elems
+ * counts elements of the arena's K/V type; a float32 pooled row in a bf16
+ * arena uses two slots per value.
+ *
+ * Region bases: a cache pointer is its layer's part of page 0 ([P1 "What this
+ * changes"]); k, v, ik and pooled are such pointers into one arena.
+ *
+ * Ownership ([P2 maintainer replies: drain before anything is freed, fills on
+ * the engine stream]): the caller allocates and owns every buffer (inputs,
+ * arena, table, lengths, outputs, workspace).  The library allocates nothing,
+ * frees nothing, keeps no global state, reads no environment variable and
+ * never synchronises: all work is enqueued on `stream`.  Inputs are only read.
+ * The caller must not free, reuse or re-table pages until `stream` has drained.
+ * Structs are passed by host pointer and read only during the call.
+ *
+ * Errors: a negative status is returned before anything is enqueued when an
+ * argument is refused (the pages refuse what they cannot serve: a page size
+ * that is not a multiple of 4 [P2 "What this changes"], a run shorter than its
+ * parts [P2 commit 51f8354]).  PAGED_EHIP reports a failed launch.  Table
+ * entries are not range-checked on the device: an entry outside the arena is
+ * undefined behaviour.  Lengths, block ranges and block ids are clamped or
+ * ignored on the device as stated per call, so that no table entry past the
+ * validated extent is ever read.
+ *
+ * Numerics: every sum keeps one fixed order that depends only on a stream's
+ * own length (never on the page size, the table or the other streams), so the
+ * paged result is byte-equal to the contiguous one at any page size that holds
+ * whole rows ([P1 "What this changes": "Only addresses change; no sum changes
+ * order"]), and a stream in a batch equals the same stream alone.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum { PAGED_F32 = 0, PAGED_BF16 = 1 } paged_dtype;
+
+/* Status codes. */
+enum {
+  PAGED_OK = 0,
+  PAGED_EINVAL = -1,       /* an argument is out of range, NULL or misaligned  */
+  PAGED_EUNSUPPORTED = -2, /* a valid request this build does not serve        */
+  PAGED_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
+  PAGED_EHIP = -4          /* a HIP launch failed                               */
+};
+
+/* The pages' Pg argument ([P1 "What this changes"]). */
+typedef struct {
+  const int32_t *table;  /* device [n_streams][table_stride] arena page ids, or NULL (contiguous) */
+  int32_t table_stride;  /* entries per stream row; table_stride * page_pos >= max_len            */
+  int32_t page_pos;      /* positions a page; = cap (rows a head) when table == NULL              */
+  int64_t page_elems;    /* elements (of the arena's K/V type) a page; the stream stride when
+                            table == NULL; page_elems * element size must be a multiple of 16   */
+  int64_t reserved;      /* must be 0 (a poisoned struct is refused)                            */
+} paged_pg;
+
+/* Key and value regions of one attention layer ([P2 commit 3f5b87d]:
+   [key, value][head][position][row] inside a page). */
+typedef struct {
+  const void *k;         /* device, 16-byte aligned: the K region of page 0, [Hkv][page_pos][D] a page */
+  const void *v;         /* device, 16-byte aligned: the V region of page 0, same shape              */
+  int32_t dtype;         /* paged_dtype of K and V                                                     */
+  int32_t n_kv_heads;    /* Hkv >= 1                                                                   */
+  int32_t head_dim;      /* D; this build serves D = 256                                               */
+  int32_t reserved;      /* must be 0                                                                  */
+} paged_kv;
+
+/* ------------------------------------------------------------------------ */
+/* Dense decode ([P1 "What this changes": fn_attn_chunks' key and value tiles
+ * read through pg_at, one lookup per key per tile, key_at beside key_ids;
+ * P2 commit ce5b78d: attention partials]).
+ *
+ * For every stream s and query head h: out[s][h] = softmax(scale * K q) V over
+ * the L_s cached positions 0..L_s-1 of KV head h / (Hq / Hkv).
+ *   q        device [n_streams][n_q_heads][256], q_dtype == kv->dtype, 16-byte aligned
+ *   seq_lens device [n_streams] int32; values are clamped to [0, max_len]
+ *   max_len  host bound on every length; table_stride * page_pos >= max_len
+ *            (page_pos >= max_len when table == NULL)
+ *   out      device [n_streams][n_q_heads][256] float32; a stream of length 0 gets zeros
+ *   workspace device, >= paged_attn_decode_workspace(n_streams, n_q_heads, max_len) bytes,
+ *            16-byte aligned (split partials; contents undefined after the call)
+ * Serves n_q_heads / n_kv_heads in {1, 2, 4, 8}, head_dim 256, F32 or BF16.
+ */
+int paged_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                      const paged_kv *kv, const paged_pg *pg,
+                      const int32_t *seq_lens, int32_t n_streams, int32_t max_len,
+                      float scale, float *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t paged_attn_decode_workspace(int32_t n_streams, int32_t n_q_heads, int32_t max_len);
+
+/* ------------------------------------------------------------------------ */
+/* Chunked causal prefill for one stream ([P2 maintainer reply: paged or mixed
+ * prompt batches take the page-run path, flat ones the tensor-core attention;
+ * here one MFMA kernel serves both through pg_at]).
+ *
+ * Queries at absolute positions q_pos0 .. q_pos0+n_q-1 attend, per head, to the
+ * cached keys 0 .. p (causal != 0) or 0 .. q_pos0+n_q-1 (causal == 0); the
+ * chunk's own rows must already be stored.  The stream's table row is
+ * pg->table[0 .. table_stride-1] (pass the row's address for stream s).
+ *   q    device [n_q][n_q_heads][256] bf16 (q_dtype == PAGED_BF16 == kv->dtype)
+ *   out  device [n_q][n_q_heads][256] float32
+ *   table_stride * page_pos >= q_pos0 + n_q
+ *   workspace: >= paged_attn_prefill_workspace(n_q, n_q_heads, q_pos0 + n_q) bytes (may be 0)
+ * Serves bf16, head_dim 256, n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ */
+int paged_attn_prefill(const void *q, int32_t q_dtype, int32_t n_q, int32_t q_pos0,
+                       int32_t n_q_heads, const paged_kv *kv, const paged_pg *pg,
+                       int32_t causal, float scale, float *out,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t paged_attn_prefill_workspace(int32_t n_q, int32_t n_q_heads, int32_t kv_len);
+
+/* ------------------------------------------------------------------------ */
+/* Block pooling ([P1 "What this changes": fn_qsa_pool reads and writes through
+ * pg_at once per block of four; a page holds the pooled rows of its n/4 blocks]).
+ *
+ * For each stream s and block b in [block_begin[s], block_end[s]) (clamped to
+ * [0, max_len / 4)): pooled row b = float32(((IK[4b] + IK[4b+1]) + IK[4b+2]) + IK[4b+3]) / 4)
+ * with the sum in float64.  IK rows are [page_pos][idx_dim] a page (one row a
+ * position), pooled rows [page_pos/4][idx_dim] float32 a page, both read and
+ * written through the table.
+ *   ik      device, region base of page 0, arena_dtype elements, 16-byte aligned
+ *   pooled  device, region base of page 0, float32, 16-byte aligned
+ *   idx_dim multiple of 8, 8 .. 1024; page_pos a multiple of 4
+ */
+int paged_pool_blocks(const void *ik, void *pooled, int32_t idx_dim, int32_t arena_dtype,
+                      const paged_pg *pg, const int32_t *block_begin, const int32_t *block_end,
+                      int32_t n_streams, int32_t max_len, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Block scores and top-k selection ([P1 "What this changes": fn_qsa_scores reads
+ * pooled rows through pg_at; four-head QSA scores]).
+ *
+ * score[s][b] = sum over indexer heads h, then dimensions d, of qi[s][h][d] * pooled[s][b][d],
+ * accumulated in float64 in that order (each product is exact), for the
+ * nb_s = min(seq_lens[s], max_len) / 4 complete blocks.  Then the k blocks with
+ * the highest score (lower id first among equal scores; -0.0 == +0.0) are
+ * written ascending to out_ids[s][0 .. n-1] with n = min(k, nb_s); the rest of
+ * the row is filled with -1 and out_count[s] = n.
+ *   qi         device [n_streams][n_idx_heads][idx_dim], qi_dtype
+ *   pooled     device, pooled region base (float32 rows, see paged_pool_blocks);
+ *              arena_dtype is the arena's K/V type, which gives page_elems its byte size
+ *   out_scores optional device [n_streams][max_len/4] float64 (NULL: kept in workspace)
+ *   workspace  >= paged_topk_workspace(n_streams, max_len, k) bytes
+ * Scores are NaN-free for finite inputs; NaN scores are undefined behaviour.
+ */
+int paged_block_scores_topk(const void *qi, int32_t qi_dtype, int32_t n_idx_heads, int32_t idx_dim,
+                            const void *pooled, int32_t arena_dtype, const paged_pg *pg,
+                            const int32_t *seq_lens, int32_t n_streams, int32_t max_len, int32_t k,
+                            int32_t *out_ids, int32_t *out_count, double *out_scores,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t paged_topk_workspace(int32_t n_streams, int32_t max_len, int32_t k);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse attention over selected blocks ([P1 "Receipt": dense and sparse
+ * attention rows equal contiguous]).
+ *
+ * Like paged_attn_decode, over the positions 4b .. 4b+3 of the blocks
+ * block_ids[s][0 .. n_selected[s]-1], in list order.  With ascending ids and
+ * every block of a stream selected the result is byte-equal to dense decode.
+ * Ids outside [0, max_len/4) are skipped; n_selected is clamped to [0, k].
+ *   block_ids  device [n_streams][k] int32
+ *   n_selected device [n_streams] int32
+ *   workspace  >= paged_sparse_attn_workspace(n_streams, n_q_heads, k) bytes
+ */
+int paged_sparse_attn(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                      const paged_kv *kv, const paged_pg *pg,
+                      const int32_t *block_ids, const int32_t *n_selected, int32_t k,
+                      int32_t n_streams, int32_t max_len, float scale, float *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t paged_sparse_attn_workspace(int32_t n_streams, int32_t n_q_heads, int32_t k);
+
+/* ------------------------------------------------------------------------ */
+/* Row stores and gathers ([P1 "What this changes": fn_attn_prep stores keys,
+ * values and indexer keys through pg_at; prompt-cache saves and restores copy
+ * page runs in the contiguous layout]).
+ *
+ * paged_rows_store copies rows (s, h, p) for p in [pos_begin[s], pos_end[s])
+ * (clamped to [0, max_len)) and h < n_heads from a strided source into a
+ * region whose page part is [n_heads][page_pos][row_elems]; paged_rows_gather
+ * copies the other way.  Strides are in elements; the source (destination)
+ * row of (s, h, p) starts at s*stride_s + h*stride_h + p*stride_p.
+ * row_elems * element size must be a multiple of 16; strides and base
+ * pointers must keep every row 16-byte aligned.
+ */
+int paged_rows_store(const void *src, int64_t stride_s, int64_t stride_h, int64_t stride_p,
+                     void *region, int32_t n_heads, int32_t row_elems, int32_t dtype,
+                     const paged_pg *pg, const int32_t *pos_begin, const int32_t *pos_end,
+                     int32_t n_streams, int32_t max_len, hipStream_t stream);
+int paged_rows_gather(void *dst, int64_t stride_s, int64_t stride_h, int64_t stride_p,
+                      const void *region, int32_t n_heads, int32_t row_elems, int32_t dtype,
+                      const paged_pg *pg, const int32_t *pos_begin, const int32_t *pos_end,
+                      int32_t n_streams, int32_t max_len, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Test hook: the row addressing itself, on the device.  out[i] = the element
+ * offset of row (streams[i], heads[i], positions[i]) in a region whose page
+ * part is [H][page_pos][row_width] -- the same device function every kernel
+ * above uses.  Entries whose stream or position is negative or past the
+ * table's extent get -1.
+ */
+int paged_row_offsets(const paged_pg *pg, int32_t n_streams, int32_t row_width,
+                      const int32_t *streams, const int32_t *heads, const int32_t *positions,
+                      int64_t *out, int32_t n, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char *paged_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,59 @@
+// Device-side row addressing shared by every kernel of libpagedattn.
+//
+// pg_at follows TensorFold PR #1169 "What this changes": with no table a row is
+// the old contiguous expression; with a table it is the start of the page that
+// holds the position plus the row inside that page.  One uniform branch on the
+// table pointer is the only difference between the two forms.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace paged {
+
+// Page table as the kernels see it (byte units).
+struct PgDev {
+  const int32_t* table;  // [n_streams][stride] or nullptr
+  int32_t stride;        // entries per stream row
+  int32_t ptok;          // positions a page (cap when there is no table)
+  int64_t page_bytes;    // bytes a page (stream stride when there is no table)
+};
+
+// Byte offset of row (s, h, p) in a region whose page part is [H][ptok][row_bytes].
+__device__ __forceinline__ int64_t pg_at(const PgDev& pg, int s, int h, int p, int row_bytes) {
+  int64_t page;
+  int within;
+  if (pg.table != nullptr) {
+    const uint32_t lp = (uint32_t)p / (uint32_t)pg.ptok;
+    within = p - (int)lp * pg.ptok;
+    page = pg.table[(int64_t)s * pg.stride + lp];
+  } else {
+    page = s;
+    within = p;
+  }
+  return page * pg.page_bytes + ((int64_t)h * pg.ptok + within) * (int64_t)row_bytes;
+}
+
+// Byte offset of the pooled row of block b (positions 4b..4b+3) in a region whose
+// page part is [ptok/4][row_bytes]: the block's page, row (4b mod ptok)/4 inside it.
+__device__ __forceinline__ int64_t pool_at(const PgDev& pg, int s, int b, int row_bytes) {
+  const int p = 4 * b;
+  int64_t page;
+  int within;
+  if (pg.table != nullptr) {
+    const uint32_t lp = (uint32_t)p / (uint32_t)pg.ptok;
+    within = p - (int)lp * pg.ptok;
+    page = pg.table[(int64_t)s * pg.stride + lp];
+  } else {
+    page = s;
+    within = p;
+  }
+  return page * pg.page_bytes + (int64_t)(within >> 2) * row_bytes;
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+constexpr float NEG_INF = -__builtin_inff();
+
+}  // namespace paged

@@ -1,0 +1,110 @@
+// Launchers shared between the C-ABI host code (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace paged {
+
+constexpr int HD = 256;  // head dimension served by the attention kernels
+
+// ---- decode / sparse (decode.hip) -----------------------------------------
+struct DecArgs {
+  const void* q;          // [S][Hq][HD]
+  const char* kb;         // K region base
+  const char* vb;         // V region base
+  PgDev pg;
+  const int32_t* lens;    // dense: lengths [S]; sparse: selected block counts [S]
+  const int32_t* ids;     // sparse: block ids [S][ids_stride]; dense: nullptr
+  int32_t ids_stride;     // k
+  int32_t max_len;        // bound on lengths and on block positions
+  int32_t hq;
+  int32_t hkv;
+  float zscale;           // softmax scale * log2(e)
+  int32_t ns_max;         // split slots a (stream, head) in the workspace
+  float* part_o;          // [S][Hq][ns_max][HD]
+  float* part_ml;         // [S][Hq][ns_max][2]
+  float* out;             // [S][Hq][HD]
+};
+
+int dec_splits_max(int max_keys);
+hipError_t launch_decode(const DecArgs& a, bool bf16, int G, int n_streams, hipStream_t st);
+
+// ---- prefill (prefill.hip) ------------------------------------------------
+struct PreArgs {
+  const void* q;          // [n_q][Hq][HD] bf16
+  const char* kb;
+  const char* vb;
+  PgDev pg;               // one stream: table row 0
+  int32_t n_q;
+  int32_t q_pos0;
+  int32_t hq;
+  int32_t hkv;
+  int32_t causal;
+  float zscale;
+  float* out;             // [n_q][Hq][HD] float32
+};
+hipError_t launch_prefill(const PreArgs& a, int G, hipStream_t st);
+
+// ---- pooling, scores, top-k (qsa.hip) ---------------------------------------
+struct PoolArgs {
+  const char* ik;
+  char* pooled;
+  PgDev pg;               // page_bytes of the arena
+  const int32_t* begin;
+  const int32_t* end;
+  int32_t idx_dim;
+  int32_t max_blocks;
+  int32_t n_streams;
+};
+hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t st);
+
+struct TopkArgs {
+  const void* qi;         // [S][Hi][DI]
+  const char* pooled;
+  PgDev pg;
+  const int32_t* lens;
+  int32_t n_idx_heads;
+  int32_t idx_dim;
+  int32_t max_blocks;     // max_len / 4
+  int32_t k;
+  double* scores;         // [S][max_blocks]
+  double* qi64;           // workspace [S][Hi*DI]
+  int32_t* out_ids;       // [S][k]
+  int32_t* out_count;     // [S]
+};
+size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_external);
+hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hipStream_t st);
+
+// ---- row stores / gathers and the addressing hook (rows.hip) ----------------
+struct RowsArgs {
+  char* lin;              // strided side (source of a store, destination of a gather)
+  int64_t ss, sh, sp;     // strides in bytes
+  char* region;           // paged side
+  PgDev pg;
+  const int32_t* begin;
+  const int32_t* end;
+  int32_t n_heads;
+  int32_t row_bytes;
+  int32_t max_len;
+  int32_t n_streams;
+  int32_t gather;         // 0: lin -> region, 1: region -> lin
+};
+hipError_t launch_rows(const RowsArgs& a, hipStream_t st);
+
+struct OffArgs {
+  PgDev pg;               // page_bytes holds page_elems (element units) for this hook
+  int32_t n_streams;
+  int32_t row_width;
+  int32_t max_pos;
+  const int32_t* streams;
+  const int32_t* heads;
+  const int32_t* positions;
+  int64_t* out;
+  int32_t n;
+};
+hipError_t launch_row_offsets(const OffArgs& a, hipStream_t st);
+
+}  // namespace paged

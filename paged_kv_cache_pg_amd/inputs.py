@@ -35,9 +35,10 @@ __all__ = [
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (round to nearest, ties to even); return the 16-bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs only: u + 0x8000 never wraps below the NaN patterns
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

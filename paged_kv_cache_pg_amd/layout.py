@@ -1,0 +1,60 @@
+"""Arena layout of one attention layer inside a page (the library side's own description).
+
+TensorFold PR #1169 "What this changes": a page of n positions holds, for each
+attention layer, the keys, values and indexer keys of its n positions and the
+pooled rows of their n/4 blocks; a cache pointer is its layer's part of page 0.
+PR #1170 commit 3f5b87d gives the in-page order [key, value][head][position][row].
+This package lays a page out as
+
+    K [Hkv][n][D] | V [Hkv][n][D] | IK [n][DI] | POOL [n/4][DI] float32
+
+and hands the kernels one base pointer per region.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from .binding import ESIZE
+
+
+@dataclass(frozen=True)
+class ArenaLayout:
+    n_kv_heads: int
+    head_dim: int
+    page_pos: int
+    dtype: int            # PAGED_F32 or PAGED_BF16
+    idx_dim: int = 0
+
+    @property
+    def esize(self) -> int:
+        return ESIZE[self.dtype]
+
+    @property
+    def kv_bytes(self) -> int:
+        return self.n_kv_heads * self.page_pos * self.head_dim * self.esize
+
+    @property
+    def k_off(self) -> int:
+        return 0
+
+    @property
+    def v_off(self) -> int:
+        return self.kv_bytes
+
+    @property
+    def ik_off(self) -> int:
+        return 2 * self.kv_bytes
+
+    @property
+    def pool_off(self) -> int:
+        return self.ik_off + self.page_pos * self.idx_dim * self.esize
+
+    @property
+    def page_bytes(self) -> int:
+        if not self.idx_dim:
+            return 2 * self.kv_bytes
+        return self.pool_off + (self.page_pos // 4) * self.idx_dim * 4
+
+    @property
+    def page_elems(self) -> int:
+        return self.page_bytes // self.esize

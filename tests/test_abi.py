@@ -1,0 +1,155 @@
+"""The C ABI loads, exports every entry point its header declares, and refuses bad
+arguments before anything is enqueued (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_pg_amd as P
+from paged_kv_cache_pg_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+FAKE = 1 << 20          # a 16-byte aligned address that is never dereferenced
+MIS = FAKE + 4          # misaligned
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(paged_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert len(names) >= 13
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B._SIGS), "binding and header disagree"
+
+
+def test_strerror():
+    assert P.strerror(0) == "ok"
+    assert "workspace" in P.strerror(-3)
+    assert P.strerror(-99) == "unknown status"
+
+
+def _kv(**kw):
+    d = dict(k=FAKE, v=FAKE, dtype=B.PAGED_BF16, n_kv_heads=4, head_dim=256)
+    d.update(kw)
+    return B.make_kv(d["k"], d["v"], d["dtype"], d["n_kv_heads"], d["head_dim"])
+
+
+def _pg(table=FAKE, stride=160, ptok=256, pe=524288):
+    return B.PgStruct(table, stride, ptok, pe, 0)
+
+
+def _decode(q=FAKE, qd=B.PAGED_BF16, hq=32, kv=None, pg=None, lens=FAKE, S=4, max_len=40960, scale=0.0625,
+            out=FAKE, ws=FAKE, wsb=None):
+    kv = kv or _kv()
+    pg = pg or _pg()
+    if wsb is None:
+        wsb = P.paged_attn_decode_workspace(S, hq, max_len)
+    return B.lib().paged_attn_decode(q, qd, hq, ctypes.byref(kv), ctypes.byref(pg), lens, S, max_len, scale, out,
+                                     ws, wsb, 0)
+
+
+def test_decode_refusals():
+    E, U, W = B.PAGED_EINVAL, B.PAGED_EUNSUPPORTED, B.PAGED_EWORKSPACE
+    assert _decode(kv=_kv(head_dim=128)) == U
+    assert _decode(hq=30) == E                      # Hq % Hkv != 0
+    assert _decode(hq=64) == U                      # G = 16 not served
+    assert _decode(qd=B.PAGED_F32) == U             # q and KV types differ
+    assert _decode(qd=7) == E
+    assert _decode(pg=_pg(stride=159)) == E         # table shorter than max_len (a short run)
+    assert _decode(pg=_pg(table=0, ptok=40959)) == E  # no table: cap below max_len
+    assert _decode(pg=_pg(ptok=0)) == E
+    assert _decode(pg=_pg(pe=524288 - 1)) == E      # page not a multiple of 16 bytes / too small
+    assert _decode(pg=_pg(pe=1024)) == E            # K region does not fit in a page
+    assert _decode(q=MIS) == E
+    assert _decode(q=0) == E
+    assert _decode(out=MIS) == E
+    assert _decode(lens=0) == E
+    assert _decode(kv=_kv(k=MIS)) == E
+    assert _decode(wsb=P.paged_attn_decode_workspace(4, 32, 40960) - 1) == W
+    assert _decode(ws=0) == W
+    assert _decode(ws=MIS) == W
+    assert _decode(scale=float("nan")) == E
+    assert _decode(max_len=-1) == E
+    assert _decode(S=-1) == E
+    assert _decode(S=0, q=0, out=0, lens=0, ws=0) == B.PAGED_OK   # nothing to do, nothing touched
+
+
+def test_poisoned_structs_are_refused():
+    kv = _kv()
+    pg = _pg()
+    pg.reserved = 0xAAAAAAAAAAAAAAAA - (1 << 64)
+    assert _decode(pg=pg) == B.PAGED_EINVAL
+    kv.reserved = -1431655766  # 0xAAAAAAAA
+    assert _decode(kv=kv) == B.PAGED_EINVAL
+    raw = (ctypes.c_uint8 * ctypes.sizeof(B.PgStruct))(*([0xAA] * ctypes.sizeof(B.PgStruct)))
+    assert B.lib().paged_attn_decode(FAKE, 1, 32, ctypes.byref(_kv()), ctypes.cast(raw, ctypes.POINTER(B.PgStruct)),
+                                     FAKE, 4, 40960, 0.0625, FAKE, FAKE, 1 << 30, 0) == B.PAGED_EINVAL
+
+
+def test_workspace_sizes():
+    # 4 streams x 32 heads x 40 splits x (256 + 2) floats
+    assert P.paged_attn_decode_workspace(4, 32, 40960) == 4 * 32 * 40 * 258 * 4
+    assert P.paged_attn_decode_workspace(1, 8, 300) == 1 * 8 * 2 * 258 * 4
+    assert P.paged_attn_decode_workspace(0, 8, 300) == 0
+    assert P.paged_sparse_attn_workspace(3, 32, 512) == 3 * 32 * 8 * 258 * 4
+    assert P.paged_topk_workspace(3, 131072, 512) == 3 * 2048 * 8 + 3 * 32768 * 8
+
+
+def test_sparse_pool_topk_refusals():
+    E = B.PAGED_EINVAL
+    kv, pg = _kv(), _pg(ptok=254, pe=4 * 254 * 256 * 2)
+    L = B.lib()
+    ws = P.paged_sparse_attn_workspace(3, 32, 512)
+    # page size not a multiple of 4 (the pages' rule for n)
+    assert L.paged_sparse_attn(FAKE, 1, 32, ctypes.byref(kv), ctypes.byref(_pg(ptok=254, stride=600)), FAKE, FAKE,
+                               512, 3, 131072, 0.0625, FAKE, FAKE, ws, 0) == E
+    assert L.paged_sparse_attn(FAKE, 1, 32, ctypes.byref(kv), ctypes.byref(_pg(stride=512)), FAKE, FAKE, 0, 3,
+                               131072, 0.0625, FAKE, FAKE, ws, 0) == E           # k < 1
+    assert L.paged_pool_blocks(FAKE, FAKE, 128, 1, ctypes.byref(pg), FAKE, FAKE, 3, 131072, 0) == E
+    assert L.paged_pool_blocks(FAKE, FAKE, 100, 1, ctypes.byref(_pg(stride=512)), FAKE, FAKE, 3, 131072, 0) == E
+    pg5 = _pg(stride=512, pe=573440)
+    assert L.paged_pool_blocks(FAKE, MIS, 128, 1, ctypes.byref(pg5), FAKE, FAKE, 3, 131072, 0) == E
+    wt = P.paged_topk_workspace(3, 131072, 512)
+    assert L.paged_block_scores_topk(FAKE, 1, 4, 128, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 0, FAKE, FAKE,
+                                     0, FAKE, wt, 0) == E                            # k = 0
+    assert L.paged_block_scores_topk(FAKE, 1, 32, 128, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 512, FAKE,
+                                     FAKE, 0, FAKE, wt, 0) == E                      # 32 x 128 > 2048
+    assert L.paged_block_scores_topk(FAKE, 1, 4, 128, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 512, FAKE, FAKE,
+                                     0, FAKE, wt - 8, 0) == B.PAGED_EWORKSPACE
+
+
+def test_rows_and_offsets_refusals():
+    E = B.PAGED_EINVAL
+    L = B.lib()
+    pg = _pg(stride=10, ptok=16, pe=4 * 16 * 256 * 2)
+    assert L.paged_rows_store(FAKE, 0, 0, 256, FAKE, 4, 255, 1, ctypes.byref(pg), FAKE, FAKE, 1, 160, 0) == E
+    assert L.paged_rows_store(FAKE, 0, 0, 4, FAKE, 4, 256, 1, ctypes.byref(pg), FAKE, FAKE, 1, 160, 0) == E
+    assert L.paged_rows_store(FAKE, 0, 0, 256, FAKE, 9, 256, 1, ctypes.byref(pg), FAKE, FAKE, 1, 160, 0) == E
+    assert L.paged_rows_store(FAKE, 0, 0, 256, FAKE, 4, 256, 1, ctypes.byref(pg), FAKE, FAKE, 1, 161, 0) == E
+    assert L.paged_rows_gather(FAKE, 0, 0, 256, FAKE, 4, 256, 1, ctypes.byref(pg), 0, FAKE, 1, 160, 0) == E
+    bad = _pg()
+    bad.reserved = 1
+    assert L.paged_row_offsets(ctypes.byref(bad), 1, 256, FAKE, FAKE, FAKE, FAKE, 10, 0) == E
+    assert L.paged_row_offsets(ctypes.byref(_pg()), 1, 256, FAKE, FAKE, FAKE, FAKE, 0, 0) == B.PAGED_OK
+
+
+def test_prefill_refusals():
+    E, U = B.PAGED_EINVAL, B.PAGED_EUNSUPPORTED
+    L = B.lib()
+    kv = _kv()
+    pg = _pg(stride=32)
+    assert L.paged_attn_prefill(FAKE, 0, 2048, 6144, 32, ctypes.byref(_kv(dtype=0)), ctypes.byref(pg), 1, 0.0625,
+                                FAKE, 0, 0, 0) == U
+    assert L.paged_attn_prefill(FAKE, 1, 2048, 6145, 32, ctypes.byref(kv), ctypes.byref(pg), 1, 0.0625, FAKE, 0, 0,
+                                0) == E     # table too short for q_pos0 + n_q
+    assert L.paged_attn_prefill(FAKE, 1, -1, 0, 32, ctypes.byref(kv), ctypes.byref(pg), 1, 0.0625, FAKE, 0, 0, 0) == E
+    assert L.paged_attn_prefill(MIS, 1, 2048, 0, 32, ctypes.byref(kv), ctypes.byref(pg), 1, 0.0625, FAKE, 0, 0,
+                                0) == E

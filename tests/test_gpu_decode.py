@@ -1,0 +1,160 @@
+"""GPU parity of dense decode (paged_attn_decode) with the float64 oracle.
+
+Bar (TensorFold PR #1169 "Receipt"): paged output equals contiguous bit for bit
+over three repeats, attention rows stay within a float64 bound (here 2e-3
+max-norm relative per row), guards and inputs stay intact, and the two red
+controls (a swapped table over placed pages, a planted row) fail.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import paged_kv_cache_pg_amd as P  # noqa: E402
+from paged_kv_cache_pg_amd.inputs import make_workload  # noqa: E402
+from gpu_util import Placed, decode, dev, guarded_out, out_guards_intact, rel_err_rows, TOL  # noqa: E402
+
+
+def _oracle(w, scale, streams=None):
+    q, K, V = w.as_f64("q"), w.as_f64("K"), w.as_f64("V")
+    return O.decode(q, K, V, w.lens, scale)
+
+
+def _run_case(w, scale, repeats=3):
+    pl = Placed(w, paged=True)
+    pc = Placed(w, paged=False)
+    q = dev(w.q)
+    arena_before = pl.arena_np.copy()
+    outs = []
+    for _ in range(repeats):
+        buf, out = guarded_out((w.n_streams, w.n_q_heads, w.head_dim))
+        decode(pl, q, scale, out=out)
+        torch.cuda.synchronize()
+        assert out_guards_intact(buf), "output canaries overwritten"
+        outs.append(out.cpu().numpy().copy())
+    oc = decode(pc, q, scale).cpu().numpy()
+    for o in outs:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "repeat differs"
+    assert np.array_equal(outs[0].view(np.uint32), oc.view(np.uint32)), "paged != contiguous"
+    assert pl.guards_intact() and np.array_equal(pl.arena_now(), arena_before), "arena or guards changed"
+    return pl, pc, q, outs[0]
+
+
+def test_config1_fp32_reversed_table():
+    """1 stream, 8 q / 2 KV heads, D 256, 300 positions, pages of 16 in a reversed table, fp32, scale 1/16."""
+    w = make_workload(1, [300], 16, 8, 2, dtype="f32", table_kind="reversed")
+    assert list(w.table[0]) == list(range(18, -1, -1))
+    pl, pc, q, out = _run_case(w, 1 / 16)
+    err = rel_err_rows(out, _oracle(w, 1 / 16))
+    assert err <= TOL, err
+
+
+LENS = [1, 17, 511, 4096, 8191, 9000]
+PAGES = [16, 48, 128, 256, 512]
+
+
+@pytest.mark.parametrize("ptok", PAGES)
+@pytest.mark.parametrize("L", LENS)
+def test_page_shape_sweep(L, ptok):
+    """2 streams shuffled through one arena, 16 q / 4 KV heads, bf16."""
+    w = make_workload(2, [L, L], ptok, 16, 4, dtype="bf16", table_kind="shuffled")
+    pl, pc, q, out = _run_case(w, 1 / 16)
+    err = rel_err_rows(out, _oracle(w, 1 / 16))
+    assert err <= TOL, err
+
+
+def test_mixed_pair_concurrent_equals_solo():
+    """A long and a short stream in one batch give the bytes each gives alone (PR #2244's class of bug)."""
+    w = make_workload(2, [9000, 17], 48, 16, 4, dtype="bf16", table_kind="shuffled")
+    pl, pc, q, out = _run_case(w, 1 / 16)
+    assert rel_err_rows(out, _oracle(w, 1 / 16)) <= TOL
+    for s in range(2):
+        # the same stream alone: its own table row, its own length, a batch of one
+        table1 = pl.table[s:s + 1].contiguous()
+        pg1 = P.make_pg(table1, w.page_pos, pl.lay.page_elems)
+        ws = torch.empty(P.paged_attn_decode_workspace(1, 16, w.lens[s]), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((1, 16, 256), dtype=torch.float32, device="cuda")
+        P.paged_attn_decode(q[s:s + 1].contiguous(), P.PAGED_BF16, 16, pl.kv, pg1, pl.lens[s:s + 1].contiguous(), 1,
+                            w.lens[s], 1 / 16, o1, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy()[0].view(np.uint32), out[s].view(np.uint32))
+
+
+def test_red_controls():
+    """A swapped table over placed pages and a planted row must both change the output."""
+    w = make_workload(3, [600, 600], 16, 16, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    q = dev(w.q)
+    ref = decode(pl, q, 1 / 16).cpu().numpy()
+    t = pl.table.clone()
+    a, b = t[0, 3].item(), t[1, 5].item()
+    t[0, 3], t[1, 5] = b, a
+    pg2 = P.make_pg(t, w.page_pos, pl.lay.page_elems)
+    ws = torch.empty(P.paged_attn_decode_workspace(2, 16, 600), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(torch.from_numpy(ref)).cuda()
+    P.paged_attn_decode(q, P.PAGED_BF16, 16, pl.kv, pg2, pl.lens, 2, 600, 1 / 16, o2, ws)
+    assert not np.array_equal(o2.cpu().numpy(), ref)
+    # planted row: flip one value row of stream 1 inside the arena
+    off = O.row_offset(w.table, 16, pl.olay.page_elems, 1, 2, 100, 256) * 2 + pl.olay.v_off
+    pl.buf[pl.guard + off: pl.guard + off + 512] = 0x3F
+    o3 = decode(pl, q, 1 / 16).cpu().numpy()
+    assert not np.array_equal(o3[1], ref[1]) and np.array_equal(o3[0], ref[0])
+
+
+def test_zero_length_and_clamp():
+    """A stream of length 0 gives zeros; lengths above max_len are clamped to it."""
+    w = make_workload(4, [0, 70, 70], 16, 8, 2, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    q = dev(w.q)
+    out = decode(pl, q, 0.0625).cpu().numpy()
+    assert np.all(out[0] == 0)
+    ref = _oracle(w, 0.0625)
+    assert rel_err_rows(out[1:], ref[1:]) <= TOL
+    lens_big = dev(np.array([0, 70, 5000], np.int32))
+    out2 = decode(pl, q, 0.0625, lens=lens_big, max_len=70).cpu().numpy()
+    assert np.array_equal(out2.view(np.uint32), out.view(np.uint32))
+
+
+def test_single_key_returns_value_row_exactly():
+    w = make_workload(5, [1, 1], 16, 8, 2, dtype="bf16", table_kind="shuffled")
+    out = decode(Placed(w), dev(w.q), 0.0625).cpu().numpy()
+    V = w.as_f64("V")
+    for s in range(2):
+        for h in range(8):
+            assert np.array_equal(out[s, h].astype(np.float64), V[s, h // 4, 0])
+
+
+def test_row_offsets_hook_bitwise():
+    w = make_workload(6, [1000, 333], 48, 8, 2, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    rng = np.random.default_rng(0)
+    n = 4096
+    st = rng.integers(0, 2, n).astype(np.int32)
+    hd = rng.integers(0, 2, n).astype(np.int32)
+    ps = np.array([rng.integers(0, w.lens[s]) for s in st], np.int32)
+    out = torch.empty(n, dtype=torch.int64, device="cuda")
+    P.paged_row_offsets(pl.pg, 2, 256, dev(st), dev(hd), dev(ps), out, n)
+    got = out.cpu().numpy()
+    want = np.array([O.row_offset(w.table, 48, pl.olay.page_elems, int(s), int(h), int(p), 256)
+                     for s, h, p in zip(st, hd, ps)])
+    assert np.array_equal(got, want)
+
+
+def test_batched_decode_full_size_sampled():
+    """4 streams x 40960 positions, pages of 256 shuffled, 32 q / 4 KV heads, bf16: paged == contiguous
+    bit for bit; sampled rows against the oracle."""
+    w = make_workload(3, [40960] * 4, 256, 32, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    pc = Placed(w, paged=False)
+    q = dev(w.q)
+    o1 = decode(pl, q, 1 / 16).cpu().numpy()
+    o2 = decode(pc, q, 1 / 16).cpu().numpy()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    qf, K, V = w.as_f64("q"), w.as_f64("K"), w.as_f64("V")
+    for s, h in [(0, 0), (1, 13), (2, 31), (3, 8)]:
+        ref = O.decode(qf[s:s + 1, h:h + 1], K[s:s + 1, h // 8:h // 8 + 1], V[s:s + 1, h // 8:h // 8 + 1],
+                       [40960], 1 / 16)
+        assert rel_err_rows(o1[s, h][None], ref[0]) <= TOL
