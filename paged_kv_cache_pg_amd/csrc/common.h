@@ -19,19 +19,21 @@ struct PgDev {
   int64_t page_bytes;    // bytes a page (stream stride when there is no table)
 };
 
-// Byte offset of row (s, h, p) in a region whose page part is [H][ptok][row_bytes].
+// The page that holds position p of stream s: its table entry, or s itself when there is no table.
+__device__ __forceinline__ int32_t pg_page(const PgDev& pg, int s, int p) {
+  if (pg.table != nullptr) return pg.table[(int64_t)s * pg.stride + (uint32_t)p / (uint32_t)pg.ptok];
+  return s;
+}
+
+// Byte offset of row (h, p) inside `page`, for a region whose page part is [H][ptok][row_bytes].
+__device__ __forceinline__ int64_t pg_offset(const PgDev& pg, int32_t page, int h, int p, int row_bytes) {
+  const int within = pg.table != nullptr ? (int)((uint32_t)p % (uint32_t)pg.ptok) : p;
+  return (int64_t)page * pg.page_bytes + ((int64_t)h * pg.ptok + within) * (int64_t)row_bytes;
+}
+
+// Byte offset of row (s, h, p): the start of the page that holds the position plus the row inside it.
 __device__ __forceinline__ int64_t pg_at(const PgDev& pg, int s, int h, int p, int row_bytes) {
-  int64_t page;
-  int within;
-  if (pg.table != nullptr) {
-    const uint32_t lp = (uint32_t)p / (uint32_t)pg.ptok;
-    within = p - (int)lp * pg.ptok;
-    page = pg.table[(int64_t)s * pg.stride + lp];
-  } else {
-    page = s;
-    within = p;
-  }
-  return page * pg.page_bytes + ((int64_t)h * pg.ptok + within) * (int64_t)row_bytes;
+  return pg_offset(pg, pg_page(pg, s, p), h, p, row_bytes);
 }
 
 // Byte offset of the pooled row of block b (positions 4b..4b+3) in a region whose

@@ -8,7 +8,7 @@
 //
 // Work decomposition (fixed by the stream's own key count n only, so a stream's
 // bytes never depend on the page size, the table or the other streams):
-//   tiles of 64 keys; tps = 4 * ceil(tiles / 160) tiles a split; split c holds
+//   tiles of 64 keys; tps = 4 * ceil(tiles / 128) tiles a split; split c holds
 //   tiles [c*tps, (c+1)*tps); wave w of the split's workgroup takes the w-th
 //   contiguous quarter of them.
 // A wave processes one tile in three phases:
@@ -29,9 +29,12 @@ constexpr int TILE = 64;
 constexpr int NWAVE = 4;
 constexpr int WGS = 64 * NWAVE;
 
+constexpr int MAX_SPLITS = 32;
+
 __host__ __device__ inline int dec_tiles(int n) { return (n + TILE - 1) / TILE; }
+// Tiles a split: a multiple of the waves a workgroup, so that a stream never has more than MAX_SPLITS splits.
 __host__ __device__ inline int dec_tps(int ntiles) {
-  const int t = (ntiles + 159) / 160;
+  const int t = (ntiles + NWAVE * MAX_SPLITS - 1) / (NWAVE * MAX_SPLITS);
   return NWAVE * (t < 1 ? 1 : t);
 }
 __host__ __device__ inline int dec_splits(int n) {
@@ -42,10 +45,17 @@ __host__ __device__ inline int dec_splits(int n) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load of streamed K/V data (read once: no reuse to keep in cache).
+__device__ __forceinline__ uint4 ld_stream(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 // Sum over a 16-lane DPP row; every lane of the row ends with the same bits.
@@ -112,6 +122,16 @@ __device__ __forceinline__ int stream_keys(const DecArgs& a, int s) {
   return min(max(v, 0), a.max_len);
 }
 
+// K and V chunks a lane holds for one 4-key step: K of tile t (16 lanes a key) and
+// V of tile t-1 (32 lanes a key, two half steps).
+template <bool BF16>
+struct StepBuf {
+  static constexpr int NCQ = (HD * (BF16 ? 2 : 4)) / 256;
+  static constexpr int NCP = (HD * (BF16 ? 2 : 4)) / 512;
+  uint4 k[NCQ];
+  uint4 v[2][NCP];
+};
+
 template <bool BF16, int G>
 __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -120,9 +140,13 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   constexpr int NCP = ROWB / 512;  // 16-byte chunks a lane in PV (32 lanes a key)
   constexpr int EPC = 16 / ES;     // elements a chunk
   constexpr int NO = NCP * EPC;    // outputs a lane a head (8)
+  constexpr int NSTEP = TILE / 4;  // 4-key steps a tile
+  constexpr int RING = 4;              // step buffers (divides NSTEP, so slots are compile-time)
+  constexpr int DEPTH = RING - 1;      // steps of K/V in flight ahead of the one computed
+  using Buf = StepBuf<BF16>;
 
-  __shared__ int64_t s_keyat[NWAVE][TILE];
-  __shared__ float s_sc[NWAVE][TILE * G];
+  __shared__ int64_t s_keyat[NWAVE][4][TILE];
+  __shared__ float s_sc[NWAVE][2][TILE * G];
   __shared__ float s_alpha[NWAVE][G];
   __shared__ float s_o[NWAVE][G][HD];
   __shared__ float s_m[NWAVE][G];
@@ -138,21 +162,56 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   if (c >= ns) return;
   const int qt = tps / NWAVE;
   const int t_begin = c * tps + w * qt;
-  const int t_end = min(t_begin + qt, nt);
+  const int T = max(0, min(t_begin + qt, nt) - t_begin);  // tiles of this wave
 
   const int j16 = lane & 15, grp = lane >> 4;
   const int j32 = lane & 31, half = lane >> 5;
   const int max_blocks = a.max_len >> 2;
 
+  // Key ids: key (tile tt, lane) is position i = (t_begin + tt) * 64 + lane (dense) or 4 * ids[i / 4] + i % 4
+  // (sparse); -1 when masked.  The id and table loads are issued early and finished later so that their
+  // latency hides behind the steps in flight; every index is clamped so each load reads valid memory.
+  auto load_id = [&](int tt) -> int {
+    if (a.ids == nullptr) return 0;
+    const int i = (t_begin + tt) * TILE + lane;
+    return a.ids[(int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0)];
+  };
+  auto key_pos = [&](int tt, int id) -> int {
+    const int i = (t_begin + tt) * TILE + lane;
+    if (i >= n) return -1;
+    if (a.ids == nullptr) return i;
+    return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
+  };
+
+  // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
+  const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * ROWB;
+
+  // Loads for step i of iteration tt: K rows of tile tt and V rows of tile tt-1.  Every load is
+  // issued (masked keys and missing tiles read the q row instead) so none sits under a branch.
+  auto load_step = [&](int tt, int i, Buf& b) {
+    {
+      const bool ok_t = tt < T;
+      const int64_t off = s_keyat[w][tt & 3][4 * i + grp];
+      const char* kp = (ok_t && off >= 0) ? a.kb + off : qrow;
+#pragma unroll
+      for (int cc = 0; cc < NCQ; ++cc) b.k[cc] = ld_stream(kp + 256 * cc + 16 * j16);
+    }
+    const bool ok_v = tt >= 1 && tt <= T;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t off = s_keyat[w][(tt - 1) & 3][4 * i + 2 * j + half];
+      const char* vp = (ok_v && off >= 0) ? a.vb + off : qrow;
+#pragma unroll
+      for (int cc = 0; cc < NCP; ++cc) b.v[j][cc] = ld_stream(vp + 512 * cc + 16 * j32);
+    }
+  };
+
   // q rows of the G query heads of KV head g: 16 dims a lane (chunks at 256*cc + 16*j16).
   uint4 qr[G][NCQ];
-  {
-    const char* qb = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * ROWB;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int cc = 0; cc < NCQ; ++cc) qr[h][cc] = *(const uint4*)(qb + h * ROWB + 256 * cc + 16 * j16);
-  }
+    for (int cc = 0; cc < NCQ; ++cc) qr[h][cc] = *(const uint4*)(qrow + h * ROWB + 256 * cc + 16 * j16);
 
   float m_run = NEG_INF, l_run = 0.f;  // for head lane % G
   float o[G][NO];
@@ -161,104 +220,104 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
 #pragma unroll
     for (int e = 0; e < NO; ++e) o[h][e] = 0.f;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    // key_ids -> key_at: one table lookup a key a tile.
+  if (T > 0) {
     {
-      const int i = t * TILE + lane;
-      int pos = -1;
-      if (i < n) {
-        if (a.ids != nullptr) {
-          const int b = a.ids[(int64_t)s * a.ids_stride + (i >> 2)];
-          if (b >= 0 && b < max_blocks) pos = 4 * b + (i & 3);
-        } else {
-          pos = i;
+      const int pos0 = key_pos(0, load_id(0));
+      s_keyat[w][0][lane] = pos0 >= 0 ? pg_at(a.pg, s, g, pos0, ROWB) : (int64_t)-1;
+    }
+    int id_next = load_id(1);
+    wave_lds_sync();
+    Buf buf[RING];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_step(0, d, buf[d]);
+
+    for (int t = 0; t <= T; ++t) {
+      const bool do_qk = t < T, do_pv = t >= 1;
+      if (do_pv) {
+        // Online softmax over tile t-1: lane handles flat entries i*64 + lane (head lane % G).
+        wave_lds_sync();
+        float* sc = s_sc[w][(t - 1) & 1];
+        float ev[G];
+        float tmax = NEG_INF;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          ev[i] = sc[i * 64 + lane];
+          tmax = fmaxf(tmax, ev[i]);
+        }
+        tmax = head_max<G>(tmax);
+        const float m_new = fmaxf(m_run, tmax);
+        float tsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const float p = (ev[i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[i] - m_new);
+          sc[i * 64 + lane] = p;
+          tsum += p;
+        }
+        tsum = head_sum<G>(tsum);
+        const float alpha = (m_run == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run = l_run * alpha + tsum;
+        m_run = m_new;
+        if (lane < G) s_alpha[w][lane] = alpha;
+        wave_lds_sync();
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float al = s_alpha[w][h];
+#pragma unroll
+          for (int e = 0; e < NO; ++e) o[h][e] *= al;
         }
       }
-      s_keyat[w][lane] = pos >= 0 ? pg_at(a.pg, s, g, pos, ROWB) : (int64_t)-1;
-    }
-    wave_lds_sync();
+      // key_ids -> key_at for tile t+1: one table lookup a key, finished four steps later
+      const int pos1 = key_pos(t + 1, id_next);
+      const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
+      id_next = load_id(t + 2);
 
-    // QK: 4 keys a step.
-#pragma unroll 4
-    for (int st = 0; st < TILE / 4; ++st) {
-      const int kk = st * 4 + grp;
-      const int64_t off = s_keyat[w][kk];
-      uint4 kr[NCQ];
-      if (off >= 0) {
-        const char* kp = a.kb + off + 16 * j16;
 #pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) kr[cc] = *(const uint4*)(kp + 256 * cc);
-      } else {
+      for (int i = 0; i < NSTEP; ++i) {
+        if (i == 4 && t + 1 < T) {
+          s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, g, pos1, ROWB) : (int64_t)-1;
+          wave_lds_sync();
+        }
+        // prefetch step i + DEPTH (possibly the first steps of the next iteration)
+        {
+          const int ii = i + DEPTH;
+          if (ii < NSTEP) load_step(t, ii, buf[ii % RING]);
+          else load_step(t + 1, ii - NSTEP, buf[ii % RING]);
+        }
+        const Buf& cur = buf[i % RING];
+        if (do_qk) {
+          float acc[G];
 #pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) kr[cc] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      float acc[G];
+          for (int h = 0; h < G; ++h) {
+            float x = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float x = 0.f;
+            for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], cur.k[cc], x);
+            acc[h] = row16_sum(x);
+          }
+          float v = acc[0];
 #pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], kr[cc], x);
-        acc[h] = row16_sum(x);
-      }
-      float v = acc[0];
+          for (int h = 1; h < G; ++h) v = (j16 == h) ? acc[h] : v;
+          const int kk = 4 * i + grp;
+          const bool valid = s_keyat[w][t & 3][kk] >= 0;
+          if (j16 < G) s_sc[w][t & 1][kk * G + j16] = valid ? v * a.zscale : NEG_INF;
+        }
+        if (do_pv) {
+          const float* pp = s_sc[w][(t - 1) & 1];
 #pragma unroll
-      for (int h = 1; h < G; ++h) v = (j16 == h) ? acc[h] : v;
-      if (j16 < G) s_sc[w][kk * G + j16] = (off >= 0) ? v * a.zscale : NEG_INF;
-    }
-    wave_lds_sync();
-
-    // Online softmax over the tile: lane handles flat entries i*64 + lane (head lane % G).
-    float ev[G];
-    float tmax = NEG_INF;
+          for (int j = 0; j < 2; ++j) {
+            const int kk = 4 * i + 2 * j + half;
+            float vf[NO];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      ev[i] = s_sc[w][i * 64 + lane];
-      tmax = fmaxf(tmax, ev[i]);
-    }
-    tmax = head_max<G>(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    float tsum = 0.f;
+            for (int cc = 0; cc < NCP; ++cc) unpack16<BF16>(cur.v[j][cc], vf + cc * EPC);
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float p = (ev[i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[i] - m_new);
-      s_sc[w][i * 64 + lane] = p;
-      tsum += p;
-    }
-    tsum = head_sum<G>(tsum);
-    const float alpha = (m_run == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run = l_run * alpha + tsum;
-    m_run = m_new;
-    if (lane < G) s_alpha[w][lane] = alpha;
-    wave_lds_sync();
-
-    // PV: 2 keys a step.
+            for (int h = 0; h < G; ++h) {
+              const float p = pp[kk * G + h];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = s_alpha[w][h];
-#pragma unroll
-      for (int e = 0; e < NO; ++e) o[h][e] *= al;
-    }
-#pragma unroll 4
-    for (int st = 0; st < TILE / 2; ++st) {
-      const int kk = st * 2 + half;
-      const int64_t off = s_keyat[w][kk];
-      float vf[NO];
-      if (off >= 0) {
-        const char* vp = a.vb + off + 16 * j32;
-#pragma unroll
-        for (int cc = 0; cc < NCP; ++cc) unpack16<BF16>(*(const uint4*)(vp + 512 * cc), vf + cc * EPC);
-      } else {
-#pragma unroll
-        for (int e = 0; e < NO; ++e) vf[e] = 0.f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = s_sc[w][kk * G + h];
-#pragma unroll
-        for (int e = 0; e < NO; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+              for (int e = 0; e < NO; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+            }
+          }
+        }
       }
     }
-    wave_lds_sync();
   }
 
   // Even and odd keys were accumulated by the two half waves: add them.
@@ -307,21 +366,40 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   }
 }
 
+// Merge a (stream, head)'s split partials in split order; thread d owns dimension d.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
+  __shared__ float s_scale[MAX_SPLITS];
+  __shared__ float s_L;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int n = stream_keys(a, s);
   const int ns = dec_splits(n);
   float* outp = a.out + ((int64_t)s * a.hq + h) * HD;
-  const int64_t row0 = ((int64_t)s * a.hq + h) * a.ns_max;
-  float M = NEG_INF;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, a.part_ml[(row0 + c) * 2]);
-  float O = 0.f, L = 0.f;
-  for (int c = 0; c < ns; ++c) {
-    const float mc = a.part_ml[(row0 + c) * 2];
-    const float sc = (mc == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    O += sc * a.part_o[(row0 + c) * HD + d];
-    L += sc * a.part_ml[(row0 + c) * 2 + 1];
+  if (ns == 0) {
+    outp[d] = 0.f;
+    return;
   }
+  const int64_t row0 = ((int64_t)s * a.hq + h) * a.ns_max;
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x;
+    const float mc = c < ns ? a.part_ml[(row0 + c) * 2] : NEG_INF;
+    float M = mc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float sc = (mc == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    if (c < ns) s_scale[c] = sc;
+    const float lc = c < ns ? a.part_ml[(row0 + c) * 2 + 1] : 0.f;
+    // L in split order (lane 0 walks the splits)
+    float term = sc * lc;
+    float L = 0.f;
+    for (int cc = 0; cc < ns; ++cc) L += __shfl(term, cc);
+    if (c == 0) s_L = L;
+  }
+  __syncthreads();
+  float O = 0.f;
+  const float* po = a.part_o + row0 * HD + d;
+#pragma unroll 8
+  for (int c = 0; c < ns; ++c) O += s_scale[c] * po[(int64_t)c * HD];
+  const float L = s_L;
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
 
@@ -340,7 +418,7 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
 int dec_splits_max(int max_keys) {
   const int nt = dec_tiles(max_keys);
   const int a = (nt + NWAVE - 1) / NWAVE;
-  return a < 40 ? a : 40;
+  return a < MAX_SPLITS ? a : MAX_SPLITS;
 }
 
 hipError_t launch_decode(const DecArgs& a, bool bf16, int G, int n_streams, hipStream_t st) {
