@@ -80,7 +80,7 @@ class DecodeBench:
             self.arenas.append(arena)
         self.kvs = [P.make_kv(a.data_ptr() + self.lay.k_off, a.data_ptr() + self.lay.v_off, P.PAGED_BF16, self.HKV,
                               self.D) for a in self.arenas]
-        self.ws = torch.empty(P.paged_attn_decode_workspace(self.S, self.HQ, self.L), dtype=torch.uint8,
+        self.ws = torch.zeros(P.paged_attn_decode_workspace(self.S, self.HQ, self.L), dtype=torch.uint8,
                               device="cuda")
         self.out = torch.empty((self.S, self.HQ, self.D), dtype=torch.float32, device="cuda")
         self.alg_bytes = (self.S * self.HKV * self.L * self.D * 2 * 2    # K and V rows
@@ -130,25 +130,34 @@ class DecodeBench:
 
 
 def time_steps(fn, steps: int, warmup: int):
-    """Warm-up, then per-call HIP events on the current stream plus a bracketing pair."""
+    """Warm-up, then K steps bracketed by a synchronize and a pair of HIP events on the current stream
+    (the stream the library launches on).  Returns (ms per step, wall seconds)."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+
+def time_launches(fn, n: int):
+    """Per-launch HIP event pairs around each call (the events' own packets fall between launches)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
         evs[i][0].record()
         fn(i)
         evs[i][1].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]
-    return start.elapsed_time(end) / steps, sum(per) / len(per), min(per), wall
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(per) / n, per[0], per[n // 2]
 
 
 def main():
@@ -167,7 +176,8 @@ def main():
     dec = DecodeBench()
     err = dec.check()
     log(f"decode: sampled rows within {err:.2e} of the oracle")
-    ms_step, ms_call, ms_min, wall = time_steps(dec.step, args.steps, args.warmup)
+    ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
+    ms_call, ms_min, ms_med = time_launches(dec.step, max(args.steps, 20))
     gbs = dec.alg_bytes / (ms_step * 1e-3) / 1e9
     call_gbs = dec.alg_bytes / (ms_call * 1e-3) / 1e9
     log(f"decode: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
@@ -191,7 +201,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(call_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(call_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "paged_attn_decode (split + combine)", "alg_bytes_per_launch": dec.alg_bytes,
-                     "avg_launch_us": round(ms_call * 1e3, 2), "min_launch_us": round(ms_min * 1e3, 2)},
+                     "avg_launch_us": round(ms_call * 1e3, 2), "min_launch_us": round(ms_min * 1e3, 2),
+                     "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
     }
     if not args.no_cpu_baseline:

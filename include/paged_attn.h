@@ -107,7 +107,8 @@ typedef struct {
  *            (page_pos >= max_len when table == NULL)
  *   out      device [n_streams][n_q_heads][256] float32; a stream of length 0 gets zeros
  *   workspace device, >= paged_attn_decode_workspace(n_streams, n_q_heads, max_len) bytes,
- *            16-byte aligned (split partials; contents undefined after the call)
+ *            16-byte aligned: split partials, contents undefined after the call.  Calls that
+ *            share a workspace must not overlap in time (one stream, or ordered).
  * Serves n_q_heads / n_kv_heads in {1, 2, 4, 8}, head_dim 256, F32 or BF16.
  */
 int paged_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
@@ -189,7 +190,7 @@ size_t paged_topk_workspace(int32_t n_streams, int32_t max_len, int32_t k);
  * Ids outside [0, max_len/4) are skipped; n_selected is clamped to [0, k].
  *   block_ids  device [n_streams][k] int32
  *   n_selected device [n_streams] int32
- *   workspace  >= paged_sparse_attn_workspace(n_streams, n_q_heads, k) bytes
+ *   workspace  >= paged_sparse_attn_workspace(n_streams, n_q_heads, k) bytes (as for decode)
  */
 int paged_sparse_attn(const void *q, int32_t q_dtype, int32_t n_q_heads,
                       const paged_kv *kv, const paged_pg *pg,

@@ -59,6 +59,7 @@ int group_ok(int32_t hq, int32_t hkv) {
   return PAGED_OK;
 }
 
+// Workspace: the split partials' o, then their (m, l).
 size_t dec_ws(int32_t n_streams, int32_t n_q_heads, int64_t max_keys) {
   if (n_streams <= 0 || n_q_heads <= 0 || max_keys < 0) return 0;
   int ns = dec_splits_max((int)max_keys);
@@ -108,7 +109,7 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
   a.ns_max = ns < 1 ? 1 : ns;
   const size_t rows = (size_t)n_streams * n_q_heads * a.ns_max;
   a.part_o = (float*)ws;
-  a.part_ml = (float*)((char*)ws + rows * HD * sizeof(float));
+  a.part_ml = (float*)((char*)a.part_o + rows * HD * sizeof(float));
   a.out = out;
   return hip_status(launch_decode(a, kv->dtype == PAGED_BF16, n_q_heads / kv->n_kv_heads, n_streams, stream));
 }

@@ -8,9 +8,9 @@
 //
 // Work decomposition (fixed by the stream's own key count n only, so a stream's
 // bytes never depend on the page size, the table or the other streams):
-//   tiles of 64 keys; tps = 4 * ceil(tiles / 128) tiles a split; split c holds
-//   tiles [c*tps, (c+1)*tps); wave w of the split's workgroup takes the w-th
-//   contiguous quarter of them.
+//   tiles of 64 keys; tps = 8 * ceil(tiles / 128) tiles a split (at most 16
+//   splits); split c holds tiles [c*tps, (c+1)*tps); wave w of the split's
+//   8-wave workgroup takes the w-th contiguous eighth of them.
 // A wave processes one tile in three phases:
 //   QK:   16 lanes a key, 4 keys a step; each lane holds 16 dims of q for the G
 //         query heads of the KV group and reduces its partial dots across its
@@ -25,11 +25,28 @@ namespace paged {
 
 namespace {
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef PAGED_DEC_RING
+#define PAGED_DEC_RING 4         // 4-key steps of K/V buffered a lane (bf16)
+#endif
+#ifndef PAGED_DEC_MAX_SPLITS
+#define PAGED_DEC_MAX_SPLITS 16  // splits a stream at most
+#endif
+#ifndef PAGED_DEC_WG_PER_CU
+#define PAGED_DEC_WG_PER_CU 1    // workgroups a CU the register budget is set for
+#endif
+#ifndef PAGED_DEC_NT
+#define PAGED_DEC_NT 1           // streamed K/V loads marked nontemporal
+#endif
+#ifndef PAGED_DEC_NWAVE
+#define PAGED_DEC_NWAVE 8        // waves a workgroup (a split is shared by its waves)
+#endif
+
 constexpr int TILE = 64;
-constexpr int NWAVE = 4;
+constexpr int NWAVE = PAGED_DEC_NWAVE;
 constexpr int WGS = 64 * NWAVE;
 
-constexpr int MAX_SPLITS = 32;
+constexpr int MAX_SPLITS = PAGED_DEC_MAX_SPLITS;
 
 __host__ __device__ inline int dec_tiles(int n) { return (n + TILE - 1) / TILE; }
 // Tiles a split: a multiple of the waves a workgroup, so that a stream never has more than MAX_SPLITS splits.
@@ -49,7 +66,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load of streamed K/V data (read once: no reuse to keep in cache).
 __device__ __forceinline__ uint4 ld_stream(const char* p) {
+#if PAGED_DEC_NT
   const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+#else
+  const u32x4_t v = *(const u32x4_t*)p;
+#endif
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -58,14 +79,76 @@ __device__ __forceinline__ float dppf(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
-// Sum over a 16-lane DPP row; every lane of the row ends with the same bits.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dppf<0xB1>(x);   // quad_perm(1,0,3,2): partner lane ^ 1
-  x += dppf<0x4E>(x);   // quad_perm(2,3,0,1): partner lane ^ 2
-  x += dppf<0x141>(x);  // row_half_mirror: quad q <-> quad 1-q inside each half row
-  x += dppf<0x140>(x);  // row_mirror: half row 0 <-> half row 1
-  return x;
+// Exchange halves: x keeps its lower 32 lanes and takes y's lower 32 lanes into its upper half; y gets the
+// two upper halves (gfx950 permlane swaps).  x + y then reduces x over lane pairs (l, l^32) in the lower
+// half and y in the upper half.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
 }
+// The same between rows (16 lanes) 0 and 1 and between rows 2 and 3.
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// A key's dot products are spread over 16 lanes: lane q of a quad in each of the 4 rows (quad = key).
+// Recursive halving across rows (swaps) then a butterfly inside the quad leaves, in every lane of row r,
+// the complete dots of heads  2r, 2r+1 (G = 8),  r (G = 4),  r/2 (G = 2),  0 (G = 1).
+template <int G>
+struct QkReduce {
+  static constexpr int NR = G >= 8 ? 2 : 1;  // values a lane keeps
+  __device__ static __forceinline__ void run(float (&a)[G], float (&res)[NR]) {
+    if constexpr (G == 8) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) swap32(a[k], a[k + 4]);
+      float b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = a[k] + a[k + 4];   // rows 0,1: head k; rows 2,3: head k+4
+      swap16(b[0], b[2]);
+      swap16(b[1], b[3]);
+      res[0] = b[0] + b[2];                                   // rows 0..3: heads 0, 2, 4, 6
+      res[1] = b[1] + b[3];                                   // rows 0..3: heads 1, 3, 5, 7
+    } else if constexpr (G == 4) {
+      swap32(a[0], a[2]);
+      swap32(a[1], a[3]);
+      float b0 = a[0] + a[2], b1 = a[1] + a[3];               // rows 0,1: heads 0,1; rows 2,3: heads 2,3
+      swap16(b0, b1);
+      res[0] = b0 + b1;                                       // rows 0..3: heads 0..3
+    } else if constexpr (G == 2) {
+      swap32(a[0], a[1]);
+      float b0 = a[0] + a[1], b1 = b0;                        // rows 0,1: head 0; rows 2,3: head 1
+      swap16(b0, b1);
+      res[0] = b0 + b1;
+    } else {
+      float y = a[0];
+      swap32(a[0], y);
+      float b0 = a[0] + y, b1 = b0;
+      swap16(b0, b1);
+      res[0] = b0 + b1;
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      res[k] += dppf<0xB1>(res[k]);  // quad_perm(1,0,3,2)
+      res[k] += dppf<0x4E>(res[k]);  // quad_perm(2,3,0,1)
+    }
+  }
+  // head of value k held by a lane of row r
+  __device__ static __forceinline__ int head(int r, int k) {
+    if constexpr (G == 8) return 2 * r + k;
+    else if constexpr (G == 4) return r;
+    else if constexpr (G == 2) return r >> 1;
+    else return 0;
+  }
+  // rows that write (one copy of each head)
+  __device__ static __forceinline__ bool writer_row(int r) {
+    if constexpr (G >= 4) return true;
+    else if constexpr (G == 2) return (r & 1) == 0;
+    else return r == 0;
+  }
+};
 
 template <int G>
 __device__ __forceinline__ float head_max(float v) {
@@ -133,7 +216,7 @@ struct StepBuf {
 };
 
 template <bool BF16, int G>
-__global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(DecArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int ROWB = HD * ES;    // bytes a row
   constexpr int NCQ = ROWB / 256;  // 16-byte chunks a lane in QK (16 lanes a key)
@@ -141,7 +224,7 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   constexpr int EPC = 16 / ES;     // elements a chunk
   constexpr int NO = NCP * EPC;    // outputs a lane a head (8)
   constexpr int NSTEP = TILE / 4;  // 4-key steps a tile
-  constexpr int RING = 4;              // step buffers (divides NSTEP, so slots are compile-time)
+  constexpr int RING = BF16 ? PAGED_DEC_RING : 2;  // step buffers (divides NSTEP: compile-time slots)
   constexpr int DEPTH = RING - 1;      // steps of K/V in flight ahead of the one computed
   using Buf = StepBuf<BF16>;
 
@@ -164,7 +247,9 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   const int t_begin = c * tps + w * qt;
   const int T = max(0, min(t_begin + qt, nt) - t_begin);  // tiles of this wave
 
-  const int j16 = lane & 15, grp = lane >> 4;
+  // QK: the key of a step is the quad index inside the row; the lane's dims chunk is jj (chunks jj and jj+16).
+  const int grp = (lane & 15) >> 2, row = lane >> 4;
+  const int jj = row * 4 + (lane & 3);
   const int j32 = lane & 31, half = lane >> 5;
   const int max_blocks = a.max_len >> 2;
 
@@ -194,7 +279,7 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
       const int64_t off = s_keyat[w][tt & 3][4 * i + grp];
       const char* kp = (ok_t && off >= 0) ? a.kb + off : qrow;
 #pragma unroll
-      for (int cc = 0; cc < NCQ; ++cc) b.k[cc] = ld_stream(kp + 256 * cc + 16 * j16);
+      for (int cc = 0; cc < NCQ; ++cc) b.k[cc] = ld_stream(kp + 256 * cc + 16 * jj);
     }
     const bool ok_v = tt >= 1 && tt <= T;
 #pragma unroll
@@ -206,12 +291,12 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
     }
   };
 
-  // q rows of the G query heads of KV head g: 16 dims a lane (chunks at 256*cc + 16*j16).
+  // q rows of the G query heads of KV head g: 16 dims a lane (chunks at 256*cc + 16*jj).
   uint4 qr[G][NCQ];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int cc = 0; cc < NCQ; ++cc) qr[h][cc] = *(const uint4*)(qrow + h * ROWB + 256 * cc + 16 * j16);
+    for (int cc = 0; cc < NCQ; ++cc) qr[h][cc] = *(const uint4*)(qrow + h * ROWB + 256 * cc + 16 * jj);
 
   float m_run = NEG_INF, l_run = 0.f;  // for head lane % G
   float o[G][NO];
@@ -291,14 +376,18 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
             float x = 0.f;
 #pragma unroll
             for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], cur.k[cc], x);
-            acc[h] = row16_sum(x);
+            acc[h] = x;
           }
-          float v = acc[0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) v = (j16 == h) ? acc[h] : v;
+          using R = QkReduce<G>;
+          float res[R::NR];
+          R::run(acc, res);
           const int kk = 4 * i + grp;
-          const bool valid = s_keyat[w][t & 3][kk] >= 0;
-          if (j16 < G) s_sc[w][t & 1][kk * G + j16] = valid ? v * a.zscale : NEG_INF;
+          if ((lane & 3) == 0 && R::writer_row(row)) {
+            const bool valid = s_keyat[w][t & 3][kk] >= 0;
+#pragma unroll
+            for (int k = 0; k < R::NR; ++k)
+              s_sc[w][t & 1][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
+          }
         }
         if (do_pv) {
           const float* pp = s_sc[w][(t - 1) & 1];
@@ -342,10 +431,10 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
   }
   __syncthreads();
 
-  // Merge the four waves in order; thread d owns output dimension d.
-  const int d = threadIdx.x;
+  // Merge the waves in order; a thread owns output dimension d of head h for (h, d) = idx / HD, idx % HD.
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int idx = threadIdx.x; idx < G * HD; idx += WGS) {
+    const int h = idx / HD, d = idx % HD;
     float M = NEG_INF;
 #pragma unroll
     for (int ww = 0; ww < NWAVE; ++ww) M = fmaxf(M, s_m[ww][h]);
@@ -367,6 +456,8 @@ __global__ __launch_bounds__(WGS, 2) void decode_split_kernel(DecArgs a) {
 }
 
 // Merge a (stream, head)'s split partials in split order; thread d owns dimension d.
+static_assert(MAX_SPLITS <= 64, "the combine kernel keeps one split a lane of its first wave");
+
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   __shared__ float s_scale[MAX_SPLITS];
   __shared__ float s_L;

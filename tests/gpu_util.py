@@ -83,7 +83,7 @@ def decode(pl: Placed, q: torch.Tensor, scale: float, lens=None, max_len=None, o
     S = w.n_streams
     max_len = max_len if max_len is not None else max(w.lens + [0])
     ws_bytes = P.paged_attn_decode_workspace(S, w.n_q_heads, max_len)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     if out is None:
         out = torch.empty((S, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     P.paged_attn_decode(q, DT[w.dtype], w.n_q_heads, pl.kv, pl.pg, pl.lens if lens is None else lens, S, max_len,

@@ -95,11 +95,11 @@ def test_poisoned_structs_are_refused():
 
 
 def test_workspace_sizes():
-    # 4 streams x 32 heads x 32 splits x (256 + 2) floats
-    assert P.paged_attn_decode_workspace(4, 32, 40960) == 4 * 32 * 32 * 258 * 4
-    assert P.paged_attn_decode_workspace(1, 8, 300) == 1 * 8 * 2 * 258 * 4
+    # 4 streams x 32 heads x 16 splits x (256 + 2) floats
+    assert P.paged_attn_decode_workspace(4, 32, 40960) == 4 * 32 * 16 * 258 * 4
+    assert P.paged_attn_decode_workspace(1, 8, 300) == 1 * 8 * 1 * 258 * 4
     assert P.paged_attn_decode_workspace(0, 8, 300) == 0
-    assert P.paged_sparse_attn_workspace(3, 32, 512) == 3 * 32 * 8 * 258 * 4
+    assert P.paged_sparse_attn_workspace(3, 32, 512) == 3 * 32 * 4 * 258 * 4
     assert P.paged_topk_workspace(3, 131072, 512) == 3 * 2048 * 8 + 3 * 32768 * 8
 
 

@@ -75,7 +75,7 @@ def test_mixed_pair_concurrent_equals_solo():
         # the same stream alone: its own table row, its own length, a batch of one
         table1 = pl.table[s:s + 1].contiguous()
         pg1 = P.make_pg(table1, w.page_pos, pl.lay.page_elems)
-        ws = torch.empty(P.paged_attn_decode_workspace(1, 16, w.lens[s]), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(P.paged_attn_decode_workspace(1, 16, w.lens[s]), dtype=torch.uint8, device="cuda")
         o1 = torch.empty((1, 16, 256), dtype=torch.float32, device="cuda")
         P.paged_attn_decode(q[s:s + 1].contiguous(), P.PAGED_BF16, 16, pl.kv, pg1, pl.lens[s:s + 1].contiguous(), 1,
                             w.lens[s], 1 / 16, o1, ws)
@@ -93,7 +93,7 @@ def test_red_controls():
     a, b = t[0, 3].item(), t[1, 5].item()
     t[0, 3], t[1, 5] = b, a
     pg2 = P.make_pg(t, w.page_pos, pl.lay.page_elems)
-    ws = torch.empty(P.paged_attn_decode_workspace(2, 16, 600), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(P.paged_attn_decode_workspace(2, 16, 600), dtype=torch.uint8, device="cuda")
     o2 = torch.empty_like(torch.from_numpy(ref)).cuda()
     P.paged_attn_decode(q, P.PAGED_BF16, 16, pl.kv, pg2, pl.lens, 2, 600, 1 / 16, o2, ws)
     assert not np.array_equal(o2.cpu().numpy(), ref)
@@ -158,3 +158,46 @@ def test_batched_decode_full_size_sampled():
         ref = O.decode(qf[s:s + 1, h:h + 1], K[s:s + 1, h // 8:h // 8 + 1], V[s:s + 1, h // 8:h // 8 + 1],
                        [40960], 1 / 16)
         assert rel_err_rows(o1[s, h][None], ref[0]) <= TOL
+
+
+def test_workspace_reuse_decode_and_sparse():
+    """One workspace serves many calls (decode and sparse alike); repeats give the same bytes."""
+    w = make_workload(7, [5000, 300, 9000], 48, 16, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    q = dev(w.q)
+    max_len = 9000
+    ws = torch.full((P.paged_attn_decode_workspace(3, 16, max_len),), 0xAB, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        out = torch.empty((3, 16, 256), dtype=torch.float32, device="cuda")
+        P.paged_attn_decode(q, P.PAGED_BF16, 16, pl.kv, pl.pg, pl.lens, 3, max_len, 1 / 16, out, ws)
+        ids = dev(np.tile(np.arange(8, dtype=np.int32), (3, 1)))
+        cnt = dev(np.array([8, 8, 8], np.int32))
+        sp = torch.empty_like(out)
+        P.paged_sparse_attn(q, P.PAGED_BF16, 16, pl.kv, pl.pg, ids, cnt, 8, 3, max_len, 1 / 16, sp, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    assert rel_err_rows(outs[0], _oracle(w, 1 / 16)) <= TOL
+
+
+def test_workspace_reuse_with_changing_inputs():
+    """Calls that share a workspace but read different queries and lengths each match their own oracle
+    rows: the merge never reads a partial left by an earlier call."""
+    w = make_workload(8, [4000, 4000], 48, 16, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    rng = np.random.default_rng(3)
+    from paged_kv_cache_pg_amd.inputs import f32_to_bf16_bits
+    ws = torch.zeros(P.paged_attn_decode_workspace(2, 16, 4000), dtype=torch.uint8, device="cuda")
+    K, V = w.as_f64("K"), w.as_f64("V")
+    for it in range(6):
+        qb = f32_to_bf16_bits(rng.standard_normal((2, 16, 256)).astype(np.float32))
+        lens = [int(rng.integers(1, 4001)), int(rng.integers(1, 4001))]
+        out = torch.empty((2, 16, 256), dtype=torch.float32, device="cuda")
+        P.paged_attn_decode(dev(qb), P.PAGED_BF16, 16, pl.kv, pl.pg, dev(np.array(lens, np.int32)), 2, 4000, 1 / 16,
+                            out, ws)
+        torch.cuda.synchronize()
+        qf = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = O.decode(qf, K, V, lens, 1 / 16)
+        assert rel_err_rows(out.cpu().numpy(), ref) <= TOL, (it, lens)

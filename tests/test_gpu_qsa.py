@@ -58,7 +58,7 @@ def _sparse(pl, ids, cnt, k, q=None):
     w = pl.w
     S = w.n_streams
     out = torch.empty((S, HQ, 256), dtype=torch.float32, device="cuda")
-    ws = torch.empty(P.paged_sparse_attn_workspace(S, HQ, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(P.paged_sparse_attn_workspace(S, HQ, k), dtype=torch.uint8, device="cuda")
     P.paged_sparse_attn(dev(w.q) if q is None else q, P.PAGED_BF16, HQ, pl.kv, pl.pg, dev(ids), dev(cnt), k, S,
                         max(w.lens), 1 / 16, out, ws)
     torch.cuda.synchronize()
