@@ -109,32 +109,108 @@ class DecodeBench:
             worst = max(worst, float(np.max(np.abs(out[s, h] - ref)) / np.max(np.abs(ref))))
         return worst
 
-    def cpu_baseline(self):
-        """The oracle (gather through the table + float64 attention) on the whole workload."""
+    @classmethod
+    def cpu_baseline_from_scratch(cls, seed: int = 3, min_seconds: float = 10.0):
+        """The oracle (gather through the table + float64 attention) on the whole decode workload, drawn
+        again on the host, repeated until at least ``min_seconds`` of CPU work have been timed."""
         import oracle as O
-        w = self.w
-        olay = O.PageLayout(self.HKV, self.D, self.PTOK, "bf16")
+        from paged_kv_cache_pg_amd.inputs import bf16_bits_to_f32, make_workload
+        w = make_workload(seed, [cls.L] * cls.S, cls.PTOK, cls.HQ, cls.HKV, dtype="bf16", table_kind="shuffled")
+        olay = O.PageLayout(cls.HKV, cls.D, cls.PTOK, "bf16")
         arena = O.place(olay, w.table, w.n_pages, w.lens, w.K, w.V)
         qf = w.as_f64("q")
-        t0 = time.perf_counter()
-        K, V, _ = O.gather(olay, w.table, arena, w.lens)
-        from paged_kv_cache_pg_amd.inputs import bf16_bits_to_f32
-        K = bf16_bits_to_f32(K).astype("float64")
-        V = bf16_bits_to_f32(V).astype("float64")
-        O.decode(qf, K, V, w.lens, 1 / 16)
-        dt = time.perf_counter() - t0
-        kv_bytes = self.S * self.HKV * self.L * self.D * 2 * 2
-        return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
-                "sample": f"whole decode workload (4 streams x 40960 positions, 32 q / 4 KV heads): "
-                          f"gather through the table + float64 attention, {dt:.2f} s"}
+        reps, total = 0, 0.0
+        while total < min_seconds:
+            t0 = time.perf_counter()
+            K, V, _ = O.gather(olay, w.table, arena, w.lens)
+            K = bf16_bits_to_f32(K).astype("float64")
+            V = bf16_bits_to_f32(V).astype("float64")
+            O.decode(qf, K, V, w.lens, 1 / 16)
+            total += time.perf_counter() - t0
+            reps += 1
+            del K, V
+        kv_bytes = cls.S * cls.HKV * cls.L * cls.D * 2 * 2
+        return {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+                "kind": "oracle",
+                "sample": f"whole decode workload (4 streams x 40960 positions, 32 q / 4 KV heads): gather through "
+                          f"the table + float64 attention, {reps} passes in {total:.2f} s"}
+
+
+# ---------------------------------------------------------------------------
+# Chunked causal prefill (MFMA)
+# ---------------------------------------------------------------------------
+
+class PrefillBench:
+    """One stream, a prompt of N tokens processed as chunks of 2048 queries against its paged cache
+    (pages of 256 shuffled), 32 q / 4 KV heads, head dim 256, bf16; all K/V rows stored first."""
+    HQ, HKV, D, PTOK, CHUNK = 32, 4, 256, 256, 2048
+
+    def __init__(self, n_tokens: int, seed: int = 4):
+        import numpy as np
+        import torch
+        import paged_kv_cache_pg_amd as P
+        from paged_kv_cache_pg_amd.inputs import make_workload
+        self.P, self.torch, self.N = P, torch, n_tokens
+        t0 = time.time()
+        w = make_workload(seed, [n_tokens], self.PTOK, self.HQ, self.HKV, dtype="bf16", table_kind="shuffled",
+                          n_queries=n_tokens)
+        self.w = w
+        log(f"prefill {n_tokens}: workload drawn in {time.time() - t0:.1f}s")
+        lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_BF16)
+        self.table = torch.from_numpy(w.table.astype(np.int32)).cuda()
+        self.pg = P.make_pg(self.table, self.PTOK, lay.page_elems)
+        lens = torch.tensor([n_tokens], dtype=torch.int32, device="cuda")
+        begin = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.arena = torch.zeros(w.n_pages * lay.page_bytes, dtype=torch.uint8, device="cuda")
+        for name, off in (("K", lay.k_off), ("V", lay.v_off)):
+            src = torch.from_numpy(getattr(w, name).view(np.int16)).cuda()
+            P.paged_rows_store(src, self.HKV * n_tokens * self.D, n_tokens * self.D, self.D,
+                               self.arena.data_ptr() + off, self.HKV, self.D, P.PAGED_BF16, self.pg, begin, lens, 1,
+                               n_tokens)
+            torch.cuda.synchronize()
+            del src
+        self.kv = P.make_kv(self.arena.data_ptr() + lay.k_off, self.arena.data_ptr() + lay.v_off, P.PAGED_BF16,
+                            self.HKV, self.D)
+        self.q = torch.from_numpy(w.q.view(np.int16)).cuda()          # [N][Hq][D]
+        self.out = torch.empty((self.CHUNK, self.HQ, self.D), dtype=torch.float32, device="cuda")
+        self.flops = 4.0 * self.D * self.HQ * n_tokens * (n_tokens + 1) / 2   # unmasked QK^T + PV
+
+    def chunk(self, c0: int):
+        n = min(self.CHUNK, self.N - c0)
+        self.P.paged_attn_prefill(self.q[c0:c0 + n], self.P.PAGED_BF16, n, c0, self.HQ, self.kv, self.pg, True,
+                                  1 / 16, self.out)
+
+    def run(self, i: int = 0):
+        for c0 in range(0, self.N, self.CHUNK):
+            self.chunk(c0)
+
+    def check_last_chunk(self):
+        import numpy as np
+        import oracle as O
+        c0 = ((self.N - 1) // self.CHUNK) * self.CHUNK
+        self.chunk(c0)
+        self.torch.cuda.synchronize()
+        out = self.out.cpu().numpy()
+        rows = np.array([0, 1, min(self.CHUNK, self.N - c0) - 1])
+        w = self.w
+        qc = np.ascontiguousarray(w.q[c0:c0 + self.CHUNK])
+        qf = (qc.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = O.prefill(qf, w.as_f64("K")[0], w.as_f64("V")[0], c0, 1 / 16, rows=rows)
+        return float(max(np.max(np.abs(out[r] - ref[r])) / np.max(np.abs(ref[r])) for r in rows))
 
 
 def time_steps(fn, steps: int, warmup: int):
     """Warm-up, then K steps bracketed by a synchronize and a pair of HIP events on the current stream
     (the stream the library launches on).  Returns (ms per step, wall seconds)."""
     import torch
-    for i in range(warmup):
+    # at least `warmup` steps and at least 0.3 s of them, so clocks have settled after host-side work
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_w < 0.3:
         fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -174,10 +250,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     dec = DecodeBench()
-    err = dec.check()
-    log(f"decode: sampled rows within {err:.2e} of the oracle")
     ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
     ms_call, ms_min, ms_med = time_launches(dec.step, max(args.steps, 20))
+    err = dec.check()
+    log(f"decode: sampled rows within {err:.2e} of the oracle")
     gbs = dec.alg_bytes / (ms_step * 1e-3) / 1e9
     call_gbs = dec.alg_bytes / (ms_call * 1e-3) / 1e9
     log(f"decode: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
@@ -205,8 +281,24 @@ def main():
                      "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
     }
+    del dec
+    torch.cuda.empty_cache()
+    prefill = {}
+    for n_tok in (8192, 40960):
+        pb = PrefillBench(n_tok)
+        ms, _ = time_steps(pb.run, max(1, args.steps // 10), 1)
+        perr = pb.check_last_chunk()
+        tflops = pb.flops / (ms * 1e-3) / 1e12
+        prefill[str(n_tok)] = {"tokens_per_s": round(n_tok / (ms * 1e-3), 1), "ms": round(ms, 3),
+                               "chunks": (n_tok + 2047) // 2048, "alg_tflops": round(tflops, 1),
+                               "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "oracle_max_rel_err": perr}
+        log(f"prefill {n_tok}: {ms:.2f} ms, {n_tok / (ms * 1e-3):.0f} tok/s, {tflops:.0f} TFLOP/s "
+            f"({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        del pb
+        torch.cuda.empty_cache()
+    result["prefill"] = prefill
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = dec.cpu_baseline()
+        result["cpu_baseline"] = DecodeBench.cpu_baseline_from_scratch()
     print(json.dumps(result), flush=True)
 
 
