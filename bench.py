@@ -29,6 +29,21 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
+# by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
+# only for the kernel sources that were measured.
+DECODE_TRAFFIC_BYTES = 676_552_704
+DECODE_TRAFFIC_SOURCES = "5e3f1db557c9e25d"
+
+
+def _decode_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/common.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
@@ -199,6 +214,93 @@ class PrefillBench:
         return float(max(np.max(np.abs(out[r] - ref[r])) / np.max(np.abs(ref[r])) for r in rows))
 
 
+# ---------------------------------------------------------------------------
+# Block-sparse decode: pooling, scores + top-k, sparse attention
+# ---------------------------------------------------------------------------
+
+class SparseBench:
+    """3 streams x 131072 cached positions, pages of 256 shuffled; indexer keys (128 wide) pooled per
+    block of 4; 4 indexer heads score the pooled blocks; top-512 blocks; attention over their 2048 rows
+    with 32 q / 4 KV heads, head dim 256, bf16."""
+    S, L, PTOK, HQ, HKV, D, DI, HI, K = 3, 131072, 256, 32, 4, 256, 128, 4, 512
+
+    def __init__(self, seed: int = 5):
+        import numpy as np
+        import torch
+        import paged_kv_cache_pg_amd as P
+        from paged_kv_cache_pg_amd.inputs import make_workload
+        self.P, self.torch = P, torch
+        t0 = time.time()
+        w = make_workload(seed, [self.L] * self.S, self.PTOK, self.HQ, self.HKV, dtype="bf16", table_kind="shuffled",
+                          idx_dim=self.DI, n_idx_heads=self.HI)
+        self.w = w
+        log(f"sparse: workload drawn in {time.time() - t0:.1f}s")
+        lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_BF16, idx_dim=self.DI)
+        self.table = torch.from_numpy(w.table.astype(np.int32)).cuda()
+        self.pg = P.make_pg(self.table, self.PTOK, lay.page_elems)
+        self.lens = torch.tensor(w.lens, dtype=torch.int32, device="cuda")
+        zero = torch.zeros(self.S, dtype=torch.int32, device="cuda")
+        self.arena = torch.zeros(w.n_pages * lay.page_bytes, dtype=torch.uint8, device="cuda")
+        base = self.arena.data_ptr()
+        for name, off, heads, width in (("K", lay.k_off, self.HKV, self.D), ("V", lay.v_off, self.HKV, self.D),
+                                        ("IK", lay.ik_off, 1, self.DI)):
+            src = torch.from_numpy(getattr(w, name).view(np.int16)).cuda()
+            ss = heads * self.L * width
+            P.paged_rows_store(src, ss, self.L * width if heads > 1 else 0, width, base + off, heads, width,
+                               P.PAGED_BF16, self.pg, zero, self.lens, self.S, self.L)
+            torch.cuda.synchronize()
+            del src
+        self.ik, self.pooled = base + lay.ik_off, base + lay.pool_off
+        self.kv = P.make_kv(base + lay.k_off, base + lay.v_off, P.PAGED_BF16, self.HKV, self.D)
+        self.q = torch.from_numpy(w.q.view(np.int16)).cuda()
+        self.qi = torch.from_numpy(w.qI.view(np.int16)).cuda()
+        self.b0 = zero
+        self.b1 = torch.full((self.S,), self.L // 4, dtype=torch.int32, device="cuda")
+        self.ids = torch.empty((self.S, self.K), dtype=torch.int32, device="cuda")
+        self.cnt = torch.empty(self.S, dtype=torch.int32, device="cuda")
+        self.scores = torch.empty((self.S, self.L // 4), dtype=torch.float64, device="cuda")
+        self.tws = torch.empty(P.paged_topk_workspace(self.S, self.L, self.K), dtype=torch.uint8, device="cuda")
+        self.sws = torch.empty(P.paged_sparse_attn_workspace(self.S, self.HQ, self.K), dtype=torch.uint8,
+                               device="cuda")
+        self.out = torch.empty((self.S, self.HQ, self.D), dtype=torch.float32, device="cuda")
+        nb = self.S * (self.L // 4)
+        self.bytes_pool = self.S * self.L * self.DI * 2 + nb * self.DI * 4
+        self.bytes_scores = nb * self.DI * 4 + self.qi.numel() * 2 + nb * 8 + self.S * self.K * 4
+        self.bytes_sparse = self.S * self.HKV * 4 * self.K * self.D * 2 * 2 + self.q.numel() * 2 + self.out.numel() * 4
+
+    def pool(self, i=0):
+        self.P.paged_pool_blocks(self.ik, self.pooled, self.DI, self.P.PAGED_BF16, self.pg, self.b0, self.b1, self.S,
+                                 self.L)
+
+    def scores_topk(self, i=0):
+        self.P.paged_block_scores_topk(self.qi, self.P.PAGED_BF16, self.HI, self.DI, self.pooled, self.P.PAGED_BF16,
+                                       self.pg, self.lens, self.S, self.L, self.K, self.ids, self.cnt, self.scores,
+                                       self.tws)
+
+    def sparse(self, i=0):
+        self.P.paged_sparse_attn(self.q, self.P.PAGED_BF16, self.HQ, self.kv, self.pg, self.ids, self.cnt, self.K,
+                                 self.S, self.L, 1 / 16, self.out, self.sws)
+
+    def check(self):
+        """Top-k ids of stream 0 against the oracle (bit for bit), one sparse row within 2e-3."""
+        import numpy as np
+        import oracle as O
+        self.pool(); self.scores_topk(); self.sparse()
+        self.torch.cuda.synchronize()
+        w = self.w
+        pooled = O.pool(w.as_f64("IK")[:1], w.lens[:1])[0]
+        want = O.topk(O.scores(w.as_f64("qI")[0], pooled), self.K)
+        ids = self.ids.cpu().numpy()[0]
+        ok = bool(np.array_equal(ids, want))
+        pos = np.array([4 * b + j for b in want for j in range(4)])
+        Ks = (w.K[0:1][:, :, pos].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        Vs = (w.V[0:1][:, :, pos].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = O.decode(w.as_f64("q")[0:1], Ks, Vs, [len(pos)], 1 / 16)[0]
+        out = self.out.cpu().numpy()[0]
+        err = float(np.max(np.max(np.abs(out - ref), axis=1) / np.max(np.abs(ref), axis=1)))
+        return ok, err
+
+
 def time_steps(fn, steps: int, warmup: int):
     """Warm-up, then K steps bracketed by a synchronize and a pair of HIP events on the current stream
     (the stream the library launches on).  Returns (ms per step, wall seconds)."""
@@ -236,19 +338,7 @@ def time_launches(fn, n: int):
     return sum(per) / n, per[0], per[n // 2]
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-
+def run_decode(args):
     dec = DecodeBench()
     ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
     ms_call, ms_min, ms_med = time_launches(dec.step, max(args.steps, 20))
@@ -257,32 +347,23 @@ def main():
     gbs = dec.alg_bytes / (ms_step * 1e-3) / 1e9
     call_gbs = dec.alg_bytes / (ms_call * 1e-3) / 1e9
     log(f"decode: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
-    result = {
-        "metric": "paged decode KV GB/s (% of HBM peak) and prefill tokens/s at 40960 ctx",
+    out = {
         "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "batched paged decode: 4 streams x 40960 cached positions, pages of 256 shuffled in "
-                               "one arena, 32 q / 4 KV heads, head dim 256, bf16 K/V/q, fp32 accumulation",
-                   "streams": 4, "seq_len": 40960, "page_pos": 256, "q_heads": 32, "kv_heads": 4, "head_dim": 256,
-                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(call_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(call_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": DECODE_TRAFFIC_BYTES if _decode_sources_hash() == DECODE_TRAFFIC_SOURCES else None,
                      "kernel": "paged_attn_decode (split + combine)", "alg_bytes_per_launch": dec.alg_bytes,
                      "avg_launch_us": round(ms_call * 1e3, 2), "min_launch_us": round(ms_min * 1e3, 2),
                      "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
     }
     del dec
-    torch.cuda.empty_cache()
+    return out
+
+
+def run_prefill(args):
+    import torch
     prefill = {}
     for n_tok in (8192, 40960):
         pb = PrefillBench(n_tok)
@@ -296,8 +377,72 @@ def main():
             f"({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
         del pb
         torch.cuda.empty_cache()
-    result["prefill"] = prefill
-    if not args.no_cpu_baseline:
+    return prefill
+
+
+def run_sparse(args):
+    sb = SparseBench()
+    sparse = {}
+    total_us = 0.0
+    for name, fn, nbytes in (("pool_blocks", sb.pool, sb.bytes_pool), ("scores_topk", sb.scores_topk, sb.bytes_scores),
+                             ("sparse_attn", sb.sparse, sb.bytes_sparse)):
+        ms, _ = time_steps(fn, args.steps, args.warmup)
+        sparse[name] = {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        if name != "pool_blocks":
+            total_us += ms * 1e3
+        log(f"sparse {name}: {ms * 1e3:.1f} us, {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    ids_ok, serr = sb.check()
+    sparse["decode_total_us"] = round(total_us, 2)
+    sparse["topk_ids_equal_oracle"] = ids_ok
+    sparse["oracle_max_rel_err"] = serr
+    log(f"sparse: scores + top-k + attention {total_us:.1f} us; ids == oracle: {ids_ok}; err {serr:.2e}")
+    del sb
+    return sparse
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "sparse"], default=None,
+                    help="run one row only (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    result = {
+        "metric": "paged decode KV GB/s (% of HBM peak) and prefill tokens/s at 40960 ctx",
+        "value": None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "batched paged decode: 4 streams x 40960 cached positions, pages of 256 shuffled in "
+                               "one arena, 32 q / 4 KV heads, head dim 256, bf16 K/V/q, fp32 accumulation",
+                   "streams": 4, "seq_len": 40960, "page_pos": 256, "q_heads": 32, "kv_heads": 4, "head_dim": 256,
+                   "parallelism": "single GPU"},
+    }
+    if args.only in (None, "decode"):
+        result.update(run_decode(args))
+        torch.cuda.empty_cache()
+    if args.only in (None, "prefill"):
+        result["prefill"] = run_prefill(args)
+        torch.cuda.empty_cache()
+    if args.only in (None, "sparse"):
+        result["sparse"] = run_sparse(args)
+        torch.cuda.empty_cache()
+    if args.only is None and not args.no_cpu_baseline:
         result["cpu_baseline"] = DecodeBench.cpu_baseline_from_scratch()
     print(json.dumps(result), flush=True)
 
