@@ -14,8 +14,7 @@ numeric worked example for these kernels):
        KV pages from the core pool" -- description and commit messages 3f5b87d
        (Seg / kv_row), ce5b78d (attention partials) and 85aeb4b (Pg / pg_at).
 
-Readings taken where the pages are silent are listed in the design doc (the
-"readings" table); each function below names the ones it relies on.
+Where the pages are silent, each function below states the reading it takes.
 
 Parity status per function:
   page_layout / row_offset / place / gather : pinned (hand-derived offsets,
@@ -48,7 +47,7 @@ class PageLayout:
     [P1 "What this changes"]: a page of n positions holds, for each attention
     layer, the keys, values and indexer keys of its n positions and the pooled
     rows of their n/4 blocks.  [P2 commit 3f5b87d]: inside a page the order is
-    [key, value][head][position][row].  Reading (S1): K [Hkv][n][D], then
+    [key, value][head][position][row].  Reading taken: K [Hkv][n][D], then
     V [Hkv][n][D], then IK [n][DI], then POOL [n/4][DI] float32.
     All offsets are in bytes.
     """
@@ -208,8 +207,9 @@ def decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, lens: Sequence[int], sca
     """Dense decode attention, float64.
 
     q [S][Hq][D], K/V [S][Hkv][cap][D] (exact input values as float64).
-    Query head h reads KV head h // (Hq/Hkv) (reading S14) over all cached
-    positions 0..L-1 (reading S12).  A stream with L = 0 gives a zero row (S22).
+    Query head h reads KV head h // (Hq/Hkv) over all cached positions 0..L-1
+    (the current token is already stored).  A stream with L = 0 gives a zero
+    row.  (The pages fix none of these three points; these are the readings.)
     [P1 "What this changes"]: fn_attn_chunks produces the dense attention rows.
     """
     S, Hq, D = q.shape
@@ -233,7 +233,7 @@ def prefill(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos0: int, scale: flo
 
     q [Nq][Hq][D] are the queries at absolute positions q_pos0 .. q_pos0+Nq-1;
     K/V [Hkv][cap][D] hold positions 0 .. q_pos0+Nq-1 (stored before the chunk).
-    Query at position p attends to keys j <= p (reading S13); without the mask
+    Query at position p attends to keys j <= p (the causal reading); without the mask
     to every key 0 .. q_pos0+Nq-1.  ``rows`` limits the work to some query rows
     (the result still has Nq rows; others are zero).
     """
@@ -263,7 +263,7 @@ def sparse(q: np.ndarray, K: np.ndarray, V: np.ndarray, block_ids: Sequence[Sequ
 
     Block b covers positions 4b .. 4b+3 ([P1 "What this changes"]: pooled rows
     of blocks of four).  The rows attended are those positions of the selected
-    blocks (reading S11: ascending); with no selected block the row is zero.
+    blocks, in ascending position order; with no selected block the row is zero.
     """
     S, Hq, D = q.shape
     Hkv = K.shape[1]
@@ -291,7 +291,9 @@ def pool(IK: np.ndarray, lens: Sequence[int]) -> list:
     IK [S][cap][DI] exact values as float64.  For b < floor(L/4):
     pooled[b] = float32(((IK[4b] + IK[4b+1]) + IK[4b+2]) + IK[4b+3]) / 4)
     with the sum in float64 (exact for bf16 rows whose exponents lie within 43
-    binades), one rounding to float32 (readings S3, S4, S5).
+    binades), one rounding to float32.  Readings: the pooled rows are means of
+    the 128-wide indexer-key rows; the sum is exact and rounded once; only
+    complete blocks are pooled.
     [P1 "What this changes"]: the pool kernel reads once per block of four and
     the page holds the pooled rows of its n/4 blocks.
     Returns a list of [nb_s][DI] float32 arrays.
@@ -310,7 +312,8 @@ def scores(qI: np.ndarray, pooled: np.ndarray) -> np.ndarray:
     indexer query with the block's pooled row, in float64.
 
     qI [Hi][DI] exact values (float64), pooled [nb][DI] float32.
-    Accumulation order (reading S7): one float64 accumulator per block, terms
+    Accumulation order (the pages fix none; this is the reading): one float64
+    accumulator per block, terms
     added head by head and, within a head, dimension by dimension.  Every
     product of a bf16 query and a float32 pooled value is exact in float64, so
     the only roundings are those of the additions, in this order.
@@ -328,7 +331,8 @@ def topk(score: np.ndarray, k: int) -> np.ndarray:
     """Ids of the k highest scores, lowest id first among equal scores, returned ascending.
 
     Orders by (score descending, id ascending); -0.0 equals +0.0; when there are
-    no more than k blocks every block is selected (readings S8, S9, S10).
+    no more than k blocks every block is selected.  (The pages fix only
+    "lowest index wins ties"; the rest are readings.)
     """
     nb = score.shape[0]
     ids = np.arange(nb)

@@ -1,7 +1,7 @@
 """GPU parity of chunked causal prefill (paged_attn_prefill, MFMA) with the float64 oracle.
 
 A chunk of queries at positions q_pos0 .. q_pos0+n_q-1 attends, head by head, to the cached
-keys 0 .. p (reading S13: causal mask key <= query position); the chunk's own rows are stored
+keys 0 .. p (causal mask: key <= query position); the chunk's own rows are stored
 before it runs.  Checks: paged == contiguous bit for bit, repeats bit for bit, rows within
 2e-3 (max-norm relative a row) of the oracle, position 0 equal to the first value row.
 """
