@@ -71,7 +71,6 @@ struct TopkArgs {
   int32_t max_blocks;     // max_len / 4
   int32_t k;
   double* scores;         // [S][max_blocks]
-  double* qi64;           // workspace [S][Hi*DI]
   int32_t* out_ids;       // [S][k]
   int32_t* out_count;     // [S]
 };

@@ -58,98 +58,244 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Indexer queries widened to float64 once per stream (workspace).
+// Scores: a workgroup is one wave and owns 64 consecutive blocks, one a lane.
+// Each lane runs one float64 accumulator over its block's pooled row, head by
+// head and dimension by dimension (the order the definition states), with the
+// indexer queries widened to float64 in LDS and read by broadcast.  Each
+// product of a bf16 / fp32 query and a fp32 pooled value is exact in float64,
+// so the fused and unfused forms agree and the only roundings are the
+// additions, in order.
+//
+// 128-dim rows (scores_kernel128): the wave issues all 32 of its coalesced
+// 16-byte loads (two rows a load, 32 lanes a row) in two rounds of 32 rows and
+// moves the rows into each lane's registers through LDS (17 KB, so two waves
+// fit a SIMD and every block of a 3 x 32768 workload is resident at once).
+// Other widths stage 64 rows of up to 128 dims at a time.
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__global__ __launch_bounds__(256) void qi_widen_kernel(TopkArgs a) {
-  const int s = blockIdx.x;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SC_NB = 64;                 // blocks a workgroup
+constexpr int SC_DCH = 128;               // dims a staged chunk (generic kernel)
+constexpr int SC_ROWB = SC_DCH * 4 + 16;  // LDS bytes a staged row (pad: consecutive rows 4 banks apart)
+
+template <bool QBF16>
+__device__ __forceinline__ void widen_q(const TopkArgs& a, int s, double* s_q) {
   const int m = a.n_idx_heads * a.idx_dim;
-  for (int i = threadIdx.x; i < m; i += 256) {
-    double v;
-    if constexpr (BF16) {
+  for (int i = threadIdx.x; i < m; i += SC_NB) {
+    if constexpr (QBF16) {
       const uint16_t u = ((const uint16_t*)a.qi)[(int64_t)s * m + i];
-      v = (double)__uint_as_float((uint32_t)u << 16);
+      s_q[i] = (double)__uint_as_float((uint32_t)u << 16);
     } else {
-      v = (double)((const float*)a.qi)[(int64_t)s * m + i];
+      s_q[i] = (double)((const float*)a.qi)[(int64_t)s * m + i];
     }
-    a.qi64[(int64_t)s * m + i] = v;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Scores: one thread a block, one float64 accumulator, head-major then
-// dimension order (each product of a bf16/fp32 query and a fp32 pooled value
-// is exact in float64, so fused and unfused forms agree).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void scores_kernel(TopkArgs a) {
-  const int s = blockIdx.y;
+template <bool QBF16>
+__global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_stage[32 * SC_ROWB];
+  extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x 128], dynamic
+  __shared__ int64_t s_base[SC_NB];
+  const int s = blockIdx.y, lane = threadIdx.x;
   const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x * 256 >= nb) return;
-  const double* qs = a.qi64 + (int64_t)s * a.n_idx_heads * a.idx_dim;
+  const int b0 = blockIdx.x * SC_NB;
+  if (b0 >= nb) return;
+  widen_q<QBF16>(a, s, s_q);
+  const int b = b0 + lane;
+  const int nrows = min(SC_NB, nb - b0);
+  s_base[lane] = pool_at(a.pg, s, b < nb ? b : b0, 128 * 4);
+  __syncthreads();
+
+  // Rows move in two rounds of 32 (rows 0-31, then 32-63): lane (r1, ch) loads 16-byte chunk ch
+  // (dims 4ch .. 4ch+3) of rows 2i + r1.  The second round's loads are issued before the first
+  // round's rows are read out of LDS, so they are in flight meanwhile.
+  const int r1 = lane >> 5, ch = lane & 31;
+  auto load_round = [&](int rd, u32x4 (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * rd + 2 * i + r1;  // rows past nrows re-read row 0
+      v[i] = *(const u32x4*)(a.pooled + s_base[r < nrows ? r : 0] + ch * 16);
+    }
+  };
+  auto store_round = [&](const u32x4 (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *(u32x4*)(s_stage + (2 * i + r1) * SC_ROWB + ch * 16) = v[i];
+  };
+  float4 row[32];  // this lane's row: dims 4c .. 4c+3 in row[c]
+  u32x4 va[16], vb[16];
+  load_round(0, va);
+  store_round(va);
+  load_round(1, vb);
+  __syncthreads();
+  if (lane < 32) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) row[c] = *(const float4*)(s_stage + lane * SC_ROWB + c * 16);
+  }
+  __syncthreads();
+  store_round(vb);
+  __syncthreads();
+  if (lane >= 32) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) row[c] = *(const float4*)(s_stage + (lane - 32) * SC_ROWB + c * 16);
+  }
   if (b >= nb) return;
-  const float* row = (const float*)(a.pooled + pool_at(a.pg, s, b, a.idx_dim * 4));
   double acc = 0.0;
   for (int h = 0; h < a.n_idx_heads; ++h) {
-    const double* qh = qs + h * a.idx_dim;
-    for (int d = 0; d < a.idx_dim; d += 4) {
-      const float4 p = *(const float4*)(row + d);
-      acc = __fma_rn(qh[d + 0], (double)p.x, acc);
-      acc = __fma_rn(qh[d + 1], (double)p.y, acc);
-      acc = __fma_rn(qh[d + 2], (double)p.z, acc);
-      acc = __fma_rn(qh[d + 3], (double)p.w, acc);
+    const double* qh = s_q + h * 128;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      // widen the row in place each head: hoisted out of the head loop, the 128 doubles would
+      // not fit beside everything else
+      asm volatile("" : "+v"(row[c].x), "+v"(row[c].y), "+v"(row[c].z), "+v"(row[c].w));
+      const double2 q01 = *(const double2*)(qh + 4 * c);
+      const double2 q23 = *(const double2*)(qh + 4 * c + 2);
+      acc = __fma_rn(q01.x, (double)row[c].x, acc);
+      acc = __fma_rn(q01.y, (double)row[c].y, acc);
+      acc = __fma_rn(q23.x, (double)row[c].z, acc);
+      acc = __fma_rn(q23.y, (double)row[c].w, acc);
     }
   }
   a.scores[(int64_t)s * a.max_blocks + b] = acc;
 }
 
+template <bool QBF16>
+__global__ __launch_bounds__(SC_NB) void scores_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_rows[SC_NB * SC_ROWB];
+  extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x dims], dynamic
+  __shared__ int64_t s_base[SC_NB];
+  const int s = blockIdx.y, lane = threadIdx.x;
+  const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+  const int b0 = blockIdx.x * SC_NB;
+  if (b0 >= nb) return;
+  widen_q<QBF16>(a, s, s_q);
+  const int rowb = a.idx_dim * 4;
+  const int b = b0 + lane;
+  const int nrows = min(SC_NB, nb - b0);
+  s_base[lane] = pool_at(a.pg, s, b < nb ? b : b0, rowb);
+  __syncthreads();
+
+  const int nch = (a.idx_dim + SC_DCH - 1) / SC_DCH;
+  double acc = 0.0;
+  for (int h = 0; h < a.n_idx_heads; ++h) {
+    for (int c = 0; c < nch; ++c) {
+      const int d0 = c * SC_DCH, wd = min(SC_DCH, a.idx_dim - d0);
+      if (nch > 1 || h == 0) {
+        if (nch > 1) __syncthreads();  // every lane is done with the previous chunk
+        const int cpr = wd / 4;        // 16-byte chunks a row
+        for (int it = lane; it < nrows * cpr; it += SC_NB) {
+          const int r = it / cpr, cc = it - r * cpr;
+          *(u32x4*)(s_rows + r * SC_ROWB + cc * 16) = *(const u32x4*)(a.pooled + s_base[r] + (int64_t)d0 * 4 + cc * 16);
+        }
+        __syncthreads();
+      }
+      if (b < nb) {
+        const char* rw = s_rows + lane * SC_ROWB;
+        const double* qh = s_q + h * a.idx_dim + d0;
+        for (int d = 0; d < wd; d += 4) {
+          const float4 p = *(const float4*)(rw + d * 4);
+          acc = __fma_rn(qh[d + 0], (double)p.x, acc);
+          acc = __fma_rn(qh[d + 1], (double)p.y, acc);
+          acc = __fma_rn(qh[d + 2], (double)p.z, acc);
+          acc = __fma_rn(qh[d + 3], (double)p.w, acc);
+        }
+      }
+    }
+  }
+  if (b < nb) a.scores[(int64_t)s * a.max_blocks + b] = acc;
+}
+
 // ---------------------------------------------------------------------------
-// Top-k: one workgroup a stream.  Radix select of the k-th largest key over
-// order-preserving 64-bit keys (8 passes of 8 bits), then selection in id order.
+// Top-k: one workgroup a stream, item i = j * 1024 + thread for chunk j (so
+// every read is coalesced and item order is (chunk, thread) = id order).
+//  1. Coarse pass: a 4096-bin histogram of the top 12 bits of the float32
+//     order key (sign, exponent, 3 mantissa bits).  Rounding to float32 is
+//     monotone, so every item in a higher bin has a higher score; the bin T
+//     where the count from the top reaches k holds the k-th largest score.
+//  2. Refinement inside bin T on the exact 64-bit order keys: skip the bits all
+//     candidates share (from their min and max), then 8-bit digits, until the
+//     chosen digit holds exactly the keys still needed or all 64 bits are fixed.
+//  3. Compaction in id order: everything above the threshold, plus the first
+//     krem items (lowest ids) equal to it.  Ids come out ascending.
+// With at most 32 chunks the scores are read once: chunks 0-15 stay in registers,
+// chunks 16-31 in LDS.
 // ---------------------------------------------------------------------------
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_COPIES = 4;  // histogram copies a wave, picked by lane & 3, to spread same-bin atomics
+constexpr int TK_KREG = 16;         // chunks kept in registers
+constexpr int TK_KLDS = 16;         // chunks kept in LDS (with the registers: 32768 blocks)
+constexpr int TK_BINS = 4096;       // coarse bins
+constexpr int TK_SUPER = 64;        // chunks a compaction round
 
 __device__ __forceinline__ uint64_t order_key(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
   if (x == 0.0) u = 0;  // -0.0 == +0.0
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
+__device__ __forceinline__ uint32_t coarse_bin(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if (f == 0.f) u = 0;
+  u = (u >> 31) ? ~u : (u | 0x80000000u);
+  return u >> 20;
+}
 
-// Exclusive scan over the workgroup; returns the prefix, writes the total.
-__device__ __forceinline__ int wg_exclusive_scan(int v, int* s_tmp, int* total) {
+// Increments an LDS counter once for each active lane; a wave whose active lanes all
+// hit one counter adds their count with one atomic (all-equal scores would otherwise
+// serialise 64 same-address atomics an instruction).
+__device__ __forceinline__ void lds_count(uint32_t* hist, uint32_t bin) {
+  const uint64_t act = __ballot(1);
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
+  const uint64_t same = __ballot(bin == b0);
+  if (same == act) {
+    if ((threadIdx.x & 63) == (uint32_t)__builtin_ctzll(act)) atomicAdd(&hist[b0], (uint32_t)__popcll(act));
+  } else {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Exclusive scan of one 64-bit value a thread, in thread order; every thread gets the total.
+__device__ __forceinline__ uint64_t wg_scan64(uint64_t v, uint64_t* s_tmp, uint64_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
+  uint64_t x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
+    const uint64_t y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
   if (lane == 63) s_tmp[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < TK_WAVES; ++i) {
-      const int t = s_tmp[i];
-      s_tmp[i] = acc;
-      acc += t;
+  if (threadIdx.x < 64) {
+    const uint64_t t = threadIdx.x < TK_WAVES ? s_tmp[threadIdx.x] : 0;
+    uint64_t z = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t y = __shfl_up(z, off);
+      if (lane >= off) z += y;
     }
-    s_tmp[TK_WAVES] = acc;
+    if (threadIdx.x < TK_WAVES) s_tmp[threadIdx.x] = z - t;
+    if (threadIdx.x == TK_WAVES - 1) s_tmp[TK_WAVES] = z;
   }
   __syncthreads();
-  const int r = s_tmp[w] + x - v;
+  const uint64_t r = s_tmp[w] + x - v;
   *total = s_tmp[TK_WAVES];
   __syncthreads();
   return r;
 }
 
+template <bool REG>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t s_hist[TK_WAVES][TK_COPIES][256];
-  __shared__ uint32_t s_tot[256];
-  __shared__ int s_tmp[TK_WAVES + 1];
+  __shared__ uint32_t s_hist[TK_BINS];
+  __shared__ uint32_t s_cnt[2][TK_SUPER][TK_WAVES];
+  __shared__ uint64_t s_tmp[TK_WAVES + 1];
+  __shared__ uint64_t s_red[2][TK_WAVES];
+  __shared__ uint32_t s_T;
+  __shared__ int s_krem, s_done;
   __shared__ uint64_t s_prefix;
-  __shared__ int s_krem;
+  __shared__ double s_keys[REG ? TK_KLDS : 1][TK_THREADS];
 
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -163,76 +309,226 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     if (tid == 0) a.out_count[s] = nb;
     return;
   }
+  const int J = (nb + TK_THREADS - 1) / TK_THREADS;  // chunks
 
-  const int ipt = (nb + TK_THREADS - 1) / TK_THREADS;  // items a thread, contiguous ids
-  const int i0 = tid * ipt;
-  const int i1 = min(i0 + ipt, nb);
-
-  uint64_t prefix = 0, pmask = 0;
-  int krem = k;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int i = tid; i < TK_WAVES * TK_COPIES * 256; i += TK_THREADS) (&s_hist[0][0][0])[i] = 0;
-    __syncthreads();
-    for (int i = i0; i < i1; ++i) {
-      const uint64_t key = order_key(sc[i]);
-      if ((key & pmask) == prefix) atomicAdd(&s_hist[w][lane & (TK_COPIES - 1)][(key >> shift) & 0xff], 1u);
+  double reg[REG ? TK_KREG : 1];
+  if constexpr (REG) {
+#pragma unroll
+    for (int j = 0; j < TK_KREG; ++j) {
+      const int i = j * TK_THREADS + tid;
+      reg[j] = (j < J && i < nb) ? sc[i] : 0.0;
     }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t t = 0;
-      for (int ww = 0; ww < TK_WAVES; ++ww)
-        for (int cc = 0; cc < TK_COPIES; ++cc) t += s_hist[ww][cc][tid];
-      s_tot[tid] = t;
+    double t[TK_KLDS];
+#pragma unroll
+    for (int j = 0; j < TK_KLDS; ++j) {
+      const int i = (TK_KREG + j) * TK_THREADS + tid;
+      t[j] = (TK_KREG + j < J && i < nb) ? sc[i] : 0.0;
     }
-    __syncthreads();
-    if (tid == 0) {
-      int above = 0, dsel = 0;
-      for (int dgt = 255; dgt >= 0; --dgt) {
-        const int c = (int)s_tot[dgt];
-        if (above + c >= krem) { dsel = dgt; break; }
-        above += c;
+#pragma unroll
+    for (int j = 0; j < TK_KLDS; ++j) s_keys[j][tid] = t[j];
+  }
+  // f(j, i, x) for every item of this thread, chunk by chunk (LDS chunks are only this thread's own)
+  auto for_items = [&](auto&& f) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int j = 0; j < TK_KREG; ++j) {
+        const int i = j * TK_THREADS + tid;
+        if (j < J && i < nb) f(j, i, reg[j]);
       }
-      s_krem = krem - above;
-      s_prefix = prefix | ((uint64_t)dsel << shift);
+      for (int j = TK_KREG; j < J; ++j) {
+        const int i = j * TK_THREADS + tid;
+        if (i < nb) f(j, i, s_keys[j - TK_KREG][tid]);
+      }
+    } else {
+      // eight chunks' reads in flight at a time
+      for (int j8 = 0; j8 < J; j8 += 8) {
+        double t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = (j8 + u) * TK_THREADS + tid;
+          t[u] = (j8 + u < J && i < nb) ? sc[i] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = (j8 + u) * TK_THREADS + tid;
+          if (j8 + u < J && i < nb) f(j8 + u, i, t[u]);
+        }
+      }
+    }
+  };
+
+  // ---- 1. coarse histogram and the bin of the k-th largest ----
+  for (int i = tid; i < TK_BINS; i += TK_THREADS) s_hist[i] = 0;
+  __syncthreads();
+  for_items([&](int, int, double x) { lds_count(s_hist, coarse_bin(x)); });
+  __syncthreads();
+  {
+    // thread t owns bins 4095-4t .. 4092-4t (descending)
+    const int top = TK_BINS - 1 - 4 * tid;
+    uint32_t c4[4];
+    uint64_t loc = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c4[r] = s_hist[top - r];
+      loc += c4[r];
+    }
+    uint64_t tot;
+    uint64_t before = wg_scan64(loc, s_tmp, &tot);
+    if (before < (uint64_t)k && before + loc >= (uint64_t)k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (before + c4[r] >= (uint64_t)k) {
+          s_T = (uint32_t)(top - r);
+          s_krem = k - (int)before;
+          break;
+        }
+        before += c4[r];
+      }
     }
     __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    pmask |= (uint64_t)0xff << shift;
+  }
+  const uint32_t T = s_T;
+  int krem = s_krem;
+  uint64_t prefix = 0, mask = 0;
+
+  // ---- 2. refinement inside bin T on the exact keys ----
+  if ((int)s_hist[T] != krem) {
+    uint64_t kmin = ~0ull, kmax = 0;
+    for_items([&](int, int, double x) {
+      if (coarse_bin(x) == T) {
+        const uint64_t ok = order_key(x);
+        kmin = ok < kmin ? ok : kmin;
+        kmax = ok > kmax ? ok : kmax;
+      }
+    });
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t a0 = __shfl_xor(kmin, off), a1 = __shfl_xor(kmax, off);
+      kmin = a0 < kmin ? a0 : kmin;
+      kmax = a1 > kmax ? a1 : kmax;
+    }
+    if (lane == 0) {
+      s_red[0][w] = kmin;
+      s_red[1][w] = kmax;
+    }
     __syncthreads();
-  }
-  // prefix is the k-th largest key; krem of the keys equal to it are taken, lowest ids first.
-  int n_gt = 0, n_eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint64_t key = order_key(sc[i]);
-    n_gt += key > prefix;
-    n_eq += key == prefix;
-  }
-  int tot;
-  int eq_before = wg_exclusive_scan(n_eq, s_tmp, &tot);
-  int sel_cnt = 0;
-  {
-    int e = eq_before;
-    for (int i = i0; i < i1; ++i) {
-      const uint64_t key = order_key(sc[i]);
-      if (key > prefix) ++sel_cnt;
-      else if (key == prefix) { if (e < krem) ++sel_cnt; ++e; }
+    kmin = ~0ull;
+    kmax = 0;
+    for (int i = 0; i < TK_WAVES; ++i) {
+      kmin = s_red[0][i] < kmin ? s_red[0][i] : kmin;
+      kmax = s_red[1][i] > kmax ? s_red[1][i] : kmax;
+    }
+    if (kmin == kmax) {
+      prefix = kmin;
+      mask = ~0ull;  // every candidate ties: the lowest krem ids are taken
+    } else {
+      int hb = 63 - __builtin_clzll(kmin ^ kmax);  // highest bit where candidates differ
+      mask = hb == 63 ? 0ull : ~((2ull << hb) - 1);
+      prefix = kmin & mask;
+      while (true) {
+        const int lo = hb >= 7 ? hb - 7 : 0;
+        const int nd = hb - lo + 1;
+        const uint64_t dmask = ((1ull << nd) - 1) << lo;
+        __syncthreads();
+        for (int i = tid; i < 256; i += TK_THREADS) s_hist[i] = 0;
+        __syncthreads();
+        for_items([&](int, int, double x) {
+          if (coarse_bin(x) == T) {
+            const uint64_t ok = order_key(x);
+            if ((ok & mask) == prefix) lds_count(s_hist, (uint32_t)((ok & dmask) >> lo));
+          }
+        });
+        __syncthreads();
+        if (tid < 64) {
+          // wave 0 finds the digit where the count from the top reaches krem: lane l owns digits
+          // 255-4l .. 252-4l (descending); digits past 2^nd are empty
+          uint32_t c4[4], loc = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = 255 - 4 * lane - r;
+            c4[r] = d < (1 << nd) ? s_hist[d] : 0u;
+            loc += c4[r];
+          }
+          uint32_t incl = loc;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+          }
+          uint32_t above = incl - loc;
+          if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (above + c4[r] >= (uint32_t)krem) {
+                const int dsel = 255 - 4 * lane - r;
+                const int kr = krem - (int)above;
+                s_krem = kr;
+                s_prefix = prefix | ((uint64_t)dsel << lo);
+                s_done = ((int)c4[r] == kr) || lo == 0;
+                break;
+              }
+              above += c4[r];
+            }
+          }
+        }
+        __syncthreads();
+        krem = s_krem;
+        prefix = s_prefix;
+        mask |= dmask;
+        if (s_done) break;
+        hb = lo - 1;
+      }
     }
   }
-  int out_before = wg_exclusive_scan(sel_cnt, s_tmp, &tot);
-  {
-    int e = eq_before, o = out_before;
-    for (int i = i0; i < i1; ++i) {
-      const uint64_t key = order_key(sc[i]);
-      bool take = false;
-      if (key > prefix) take = true;
-      else if (key == prefix) { take = e < krem; ++e; }
-      if (take && o < k) ids[o++] = i;
+
+  // ---- 3. compaction in id order ----
+  // gt: above the threshold; eq: equal to it (the first krem of them, by id, are taken)
+  auto classify = [&](double x, bool& gt, bool& eq) {
+    const uint32_t cb = coarse_bin(x);
+    const uint64_t ok = order_key(x) & mask;
+    gt = cb > T || (cb == T && ok > prefix);
+    eq = cb == T && ok == prefix;
+  };
+  uint32_t carry_g = 0, carry_e = 0;
+  for (int j0 = 0; j0 < J; j0 += TK_SUPER) {
+    const int jn = min(TK_SUPER, J - j0);
+    for (int i = tid; i < 2 * TK_SUPER * TK_WAVES; i += TK_THREADS) (&s_cnt[0][0][0])[i] = 0;
+    __syncthreads();
+    for_items([&](int j, int, double x) {
+      if (j < j0 || j >= j0 + jn) return;
+      bool gt, eq;
+      classify(x, gt, eq);
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      if (lane == (int)__builtin_ctzll(__ballot(1))) {
+        s_cnt[0][j - j0][w] = (uint32_t)__popcll(mg);
+        s_cnt[1][j - j0][w] = (uint32_t)__popcll(me);
+      }
+    });
+    __syncthreads();
+    {
+      // table entry (chunk jj, wave ww) = thread jj * 16 + ww, in id order
+      const int jj = tid / TK_WAVES, ww = tid % TK_WAVES;
+      const uint64_t v = (uint64_t)s_cnt[0][jj][ww] | ((uint64_t)s_cnt[1][jj][ww] << 32);
+      uint64_t tot;
+      const uint64_t ex = wg_scan64(v, s_tmp, &tot);
+      s_cnt[0][jj][ww] = carry_g + (uint32_t)ex;
+      s_cnt[1][jj][ww] = carry_e + (uint32_t)(ex >> 32);
+      carry_g += (uint32_t)tot;
+      carry_e += (uint32_t)(tot >> 32);
     }
+    __syncthreads();
+    for_items([&](int j, int i, double x) {
+      if (j < j0 || j >= j0 + jn) return;
+      bool gt, eq;
+      classify(x, gt, eq);
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t eb = s_cnt[1][j - j0][w] + lanes_below(me);
+      const uint32_t pos = s_cnt[0][j - j0][w] + lanes_below(mg) + min(eb, (uint32_t)krem);
+      if ((gt || (eq && eb < (uint32_t)krem)) && pos < (uint32_t)k) ids[pos] = i;
+    });
+    __syncthreads();
   }
   if (tid == 0) a.out_count[s] = k;
-  (void)n_gt;
 }
 
 }  // namespace
@@ -251,25 +547,30 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t st) {
 
 size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_external) {
   (void)k;
-  // qi in float64 (up to 2048 values a stream) + scores unless the caller keeps them
-  size_t b = (size_t)n_streams * 2048 * sizeof(double);
-  if (!scores_external) b += (size_t)n_streams * (size_t)max_blocks * sizeof(double);
-  return b;
+  if (scores_external) return 0;
+  return (size_t)n_streams * (size_t)max_blocks * sizeof(double);
 }
 
 hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hipStream_t st) {
   if (n_streams <= 0) return hipSuccess;
-  if (qi_bf16) hipLaunchKernelGGL(qi_widen_kernel<true>, dim3(n_streams), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(qi_widen_kernel<false>, dim3(n_streams), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   if (a.max_blocks > 0) {
-    dim3 grid((a.max_blocks + 255) / 256, n_streams);
-    hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, st, a);
+    dim3 grid((a.max_blocks + SC_NB - 1) / SC_NB, n_streams);
+    const size_t qbytes = (size_t)a.n_idx_heads * a.idx_dim * sizeof(double);
+    if (a.idx_dim == 128) {
+      if (qi_bf16) hipLaunchKernelGGL(scores_kernel128<true>, grid, dim3(SC_NB), qbytes, st, a);
+      else hipLaunchKernelGGL(scores_kernel128<false>, grid, dim3(SC_NB), qbytes, st, a);
+    } else {
+      if (qi_bf16) hipLaunchKernelGGL(scores_kernel<true>, grid, dim3(SC_NB), qbytes, st, a);
+      else hipLaunchKernelGGL(scores_kernel<false>, grid, dim3(SC_NB), qbytes, st, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
+  if (a.max_blocks <= (TK_KREG + TK_KLDS) * TK_THREADS)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
   return hipGetLastError();
 }
 

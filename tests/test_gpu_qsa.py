@@ -226,3 +226,51 @@ def test_rows_store_and_gather_bitwise(ptok):
     b = back.cpu().numpy().view(np.uint16)
     for s, Ls in enumerate(w.lens):
         assert np.array_equal(b[s, :, :Ls], w.K[s, :, :Ls])
+
+
+def _topk_checked(w, pl, k, max_len=None):
+    """Pool, then scores + top-k through the C ABI; scores and ids compared bit for bit with the oracle."""
+    S = w.n_streams
+    max_len = max_len or max(w.lens)
+    b0 = dev(np.zeros(S, np.int32))
+    b1 = dev(np.array([L // 4 for L in w.lens], np.int32))
+    P.paged_pool_blocks(pl.ik, pl.pooled, w.idx_dim, P.PAGED_BF16, pl.pg, b0, b1, S, max_len)
+    ids = torch.full((S, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(S, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, max_len // 4), dtype=torch.float64, device="cuda")
+    ws = torch.empty(max(16, P.paged_topk_workspace(S, max_len, k)), dtype=torch.uint8, device="cuda")
+    P.paged_block_scores_topk(dev(w.qI), P.PAGED_BF16, w.n_idx_heads, w.idx_dim, pl.pooled, P.PAGED_BF16, pl.pg,
+                              pl.lens, S, max_len, k, ids, cnt, sc, ws)
+    torch.cuda.synchronize()
+    ids, cnt, sc = ids.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
+    pooled = O.pool(w.as_f64("IK"), w.lens)
+    for s, L in enumerate(w.lens):
+        want_sc = O.scores(w.as_f64("qI")[s], pooled[s])
+        assert np.array_equal(sc[s, :L // 4].view(np.uint64), want_sc.view(np.uint64)), s
+        want = O.topk(want_sc, k)
+        assert cnt[s] == len(want)
+        assert np.array_equal(ids[s, :len(want)], want), s
+        assert np.all(ids[s, len(want):] == -1)
+
+
+@pytest.mark.parametrize("di,hi", [(192, 3), (64, 2), (8, 1)])
+def test_scores_other_indexer_widths(di, hi):
+    """Indexer rows that are not 128 wide (staged in chunks of up to 128 dims)."""
+    w = make_workload(59, [3000, 777], 48, 2, 1, dtype="bf16", table_kind="shuffled", idx_dim=di, n_idx_heads=hi)
+    _topk_checked(w, Placed(w), 100)
+
+
+def test_topk_more_blocks_than_the_register_path():
+    """67,500 blocks in one stream: scores read from memory in every pass, ids compacted in two rounds."""
+    w = make_workload(60, [270000, 1000], 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128,
+                      n_idx_heads=4)
+    _topk_checked(w, Placed(w), 700)
+
+
+def test_topk_register_path_bound_with_a_wide_table():
+    """max_len just past the register path's 32,768 blocks while the streams are short."""
+    w = make_workload(61, [9000, 4000], 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=4)
+    stride = (131076 + 255) // 256
+    table = np.zeros((2, stride), np.int32)
+    table[:, :w.table.shape[1]] = w.table
+    _topk_checked(w, Placed(w, table=table), 512, max_len=131076)
