@@ -26,9 +26,14 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  prefill.hip: MFMA accumulators in VGPRs, so the softmax's rescale of
+# the output accumulators does not move them between AGPRs and VGPRs every tile.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature" not in l)
     if r.returncode != 0:

@@ -17,9 +17,10 @@
 //                 passes it by more than 8, so most tiles skip the rescale.
 //   O^T += V^T P^T  (MFMA; A = V^T via LDS transpose reads, B = P^T straight from the S^T
 //                 accumulators, with P split into bf16 hi + lo so P keeps ~16 bits).
-// K/V tiles are double-buffered in LDS; the next tile's rows are loaded into registers
-// while the current one is computed.  Workgroups of one KV head are spread round-robin so
-// that consecutive workgroups (one per XCD) share KV heads two XCDs apiece.
+// One barrier a tile: K and V live in two LDS buffers each; the loads of tile t+1 go from
+// global memory straight into LDS (no registers), issued at the start of iteration t into the
+// buffers tile t-1 left, and are waited for at its end.  Workgroups of one KV head are spread
+// round-robin so that consecutive workgroups (one per XCD) share KV heads two XCDs apiece.
 #include "internal.h"
 
 namespace paged {
@@ -28,8 +29,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PF_ROWS = 128;        // (query, head) rows a workgroup
@@ -37,10 +41,9 @@ constexpr int PF_WAVES = 4;         // 32 rows a wave
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KT = 64;           // keys a tile
 constexpr int ROWB = HD * 2;        // bytes a bf16 key / value row
-constexpr int K_STRIDE = ROWB + 16; // K rows in LDS: 16 rows of a fragment read land 4 banks apart
-constexpr int V_STRIDE = ROWB + 32; // V rows in LDS: the 4 rows of a transpose read land 8 banks apart
 constexpr int CH = ROWB / 16;       // 16-byte chunks a row (32)
-constexpr int LD_PER_THREAD = PF_KT * CH / PF_THREADS;  // 8 chunks of K and of V a thread a tile
+constexpr int TILEB = PF_KT * ROWB; // bytes a K or V tile in LDS (rows unpadded, chunks swizzled)
+constexpr int LD_PER_WAVE = PF_KT * CH / PF_THREADS;  // 1 KB global->LDS loads a wave a tile (8)
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a row's running max may lag behind before O is rescaled
 
 __device__ __forceinline__ void swap32(float& x, float& y) {
@@ -76,11 +79,18 @@ __device__ __forceinline__ bf16x4 lds_tr16(const char* lds_base, int byte_off) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
 }
 
+// LDS tiles hold 64 rows of 512 bytes with the 16-byte chunks of a row permuted, so that the
+// fragment reads hit distinct banks: K chunk c of row r sits at slot c ^ (r mod 16) (the 16 rows
+// of a K fragment read), V chunk c at slot c ^ 2(r mod 8) (the 8 rows x 2 chunks of 32 lanes of a
+// transpose read).
+__device__ __forceinline__ int k_slot(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int v_slot(int row, int c) { return c ^ ((row & 7) << 1); }
+
 template <int G>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   constexpr int QB = PF_ROWS / G;  // queries a workgroup
-  __shared__ __attribute__((aligned(16))) char s_k[2][PF_KT * K_STRIDE];
-  __shared__ __attribute__((aligned(16))) char s_v[2][PF_KT * V_STRIDE];
+  __shared__ __attribute__((aligned(16))) char s_k[2][TILEB];
+  __shared__ __attribute__((aligned(16))) char s_v[2][TILEB];
   __shared__ int64_t s_keyat[2][PF_KT];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, u = l >> 4, c16 = l & 15;
@@ -94,14 +104,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   const int nt = (kmax + PF_KT - 1) / PF_KT;
 
   // rows of this lane: r = 32w + 16rb + c16 -> query qi = r / G, head h = r % G
-  int prow[2];
+  int lim[2];
   bool vrow[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int r = 32 * w + 16 * rb + c16;
     const int qi = q_begin + r / G;
     vrow[rb] = qi < a.n_q;
-    prow[rb] = a.q_pos0 + qi;
+    lim[rb] = a.causal ? min(a.q_pos0 + qi + 1, kv_len) : kv_len;  // keys < lim are seen
   }
 
   // Q^T fragments (B operand): lane holds Q[row 16rb + c16][32ds + 8u .. +7]
@@ -119,37 +129,66 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     }
   }
 
-  // key_at of a tile: thread < 64 looks up one key
+  // key_at of a tile: thread < 64 looks up one key (slot tt mod 2)
   auto stage_keyat = [&](int tt) {
-    if (tid < PF_KT) {
+    if (tid < PF_KT && tt < nt) {
       const int key = tt * PF_KT + tid;
       s_keyat[tt & 1][tid] = key < kmax ? pg_at(a.pg, 0, g, key, ROWB) : (int64_t)-1;
     }
   };
-  uint4 kreg[LD_PER_THREAD], vreg[LD_PER_THREAD];
-  auto load_tile = [&](int tt) {
+  // One tile's K and V rows, global -> LDS directly (no registers): load i of wave w fills LDS
+  // slots (8w + i) * 64 + lane, i.e. rows 2(8w + i) and 2(8w + i) + 1 of each buffer, each lane
+  // fetching the chunk that belongs in its slot (the slot maps are involutions).  Keys past kmax
+  // read the first q row instead (valid, finite memory): masked keys then meet a zero weight.
+  const char* dummy = (const char*)a.q;
+  auto load_tile = [&](int tt, char* kbuf, char* vbuf) {
 #pragma unroll
-    for (int i = 0; i < LD_PER_THREAD; ++i) {
-      const int idx = i * PF_THREADS + tid;
-      const int key = idx / CH, ch = idx % CH;
-      const int64_t off = s_keyat[tt & 1][key];
-      if (off >= 0) {
-        kreg[i] = *(const uint4*)(a.kb + off + ch * 16);
-        vreg[i] = *(const uint4*)(a.vb + off + ch * 16);
-      } else {
-        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int i = 0; i < LD_PER_WAVE; ++i) {
+      const int slot = (LD_PER_WAVE * w + i) * 64 + l;
+      const int row = slot / CH, pos = slot % CH;
+      const int64_t off = s_keyat[tt & 1][row];
+      const char* ks = (off >= 0 ? a.kb + off : dummy) + k_slot(row, pos) * 16;
+      const char* vs = (off >= 0 ? a.vb + off : dummy) + v_slot(row, pos) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)ks,
+                                       (__attribute__((address_space(3))) void*)(kbuf + (LD_PER_WAVE * w + i) * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vs,
+                                       (__attribute__((address_space(3))) void*)(vbuf + (LD_PER_WAVE * w + i) * 1024),
+                                       16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  // S^T of one tile: sacc[kb][rb] holds keys 16kb + 4u + i of rows 16rb + c16.  The 32 K
+  // fragments (kb, ds) are read QK_AHEAD steps before their two MFMAs.
+  auto qk = [&](const char* kbuf, f32x4 (&sacc)[4][2]) {
+    constexpr int QK_AHEAD = 4;
+    auto kfrag = [&](int st) {
+      const int kb = st >> 3, ds = st & 7, row = 16 * kb + c16;
+      return *(const bf16x8*)(kbuf + row * ROWB + k_slot(row, 4 * ds + u) * 16);
+    };
+    bf16x8 ring[QK_AHEAD];
 #pragma unroll
-    for (int i = 0; i < LD_PER_THREAD; ++i) {
-      const int idx = i * PF_THREADS + tid;
-      const int key = idx / CH, ch = idx % CH;
-      *(uint4*)(s_k[buf] + key * K_STRIDE + ch * 16) = kreg[i];
-      *(uint4*)(s_v[buf] + key * V_STRIDE + ch * 16) = vreg[i];
+    for (int st = 0; st < QK_AHEAD; ++st) ring[st] = kfrag(st);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 32; ++st) {
+      const bf16x8 kf = ring[st % QK_AHEAD];
+      if (st + QK_AHEAD < 32) ring[st % QK_AHEAD] = kfrag(st + QK_AHEAD);
+      const int kb = st >> 3, ds = st & 7;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sacc[kb][rb], 0, 0, 0);
     }
+    // keep one fragment read a step: reads QK_AHEAD steps ahead, two MFMAs a step
+    __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
+#pragma unroll
+    for (int st = 0; st < 32 - QK_AHEAD; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QK_AHEAD, 0);
   };
 
   f32x4 oacc[16][2];
@@ -159,42 +198,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
 
-  // prologue: tile 0 into LDS, tile 1 into registers
+  // ---- prologue: K(0), V(0) into LDS ----
   stage_keyat(0);
+  stage_keyat(1);
   __syncthreads();
-  load_tile(0);
-  store_tile(0);
-  if (nt > 1) stage_keyat(1);
+  load_tile(0, s_k[0], s_v[0]);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (nt > 1) load_tile(1);
 
   for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    const char* kbuf = s_k[buf];
-    const char* vbuf = s_v[buf];
     const int k0 = t * PF_KT;
+    // K(t+1), V(t+1) into the buffers tile t-1 left; they land during this iteration and are
+    // waited for at its end
+    if (t + 1 < nt) load_tile(t + 1, s_k[(t + 1) & 1], s_v[(t + 1) & 1]);
+    stage_keyat(t + 2);
 
-    // ---- S^T = K Q^T for this tile ----
-    f32x4 sacc[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        const bf16x8 kf = *(const bf16x8*)(kbuf + (16 * kb + c16) * K_STRIDE + (32 * ds + 8 * u) * 2);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sacc[kb][rb], 0, 0, 0);
-      }
-    }
+    f32x4 s_cur[4][2];
+    qk(s_k[t & 1], s_cur);
 
-    // ---- online softmax (rows live in lane columns) ----
     bf16x8 phi[2][2], plo[2][2];  // [32-key step][rb]
     float alpha_rb[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int lim = a.causal ? min(prow[rb] + 1, kv_len) : kv_len;
       float z[4][4];
       float mx = NEG_INF;
 #pragma unroll
@@ -202,7 +227,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * kb + 4 * u + i;
-          z[kb][i] = key < lim ? sacc[kb][rb][i] * a.zscale : NEG_INF;
+          z[kb][i] = key < lim[rb] ? s_cur[kb][rb][i] * a.zscale : NEG_INF;
           mx = fmaxf(mx, z[kb][i]);
         }
       mx = col_max(mx);
@@ -224,52 +249,71 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
       rs = col_sum(rs);
       l_run[rb] = l_run[rb] * alpha + rs;
       m_run[rb] = m_new;
+      // P^T fragment of 32-key step s2: element e is key 32s2 + 16(e/4) + 4u + e%4
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = p[2 * s2 + (e >> 2)][e & 3];
-          const __bf16 hi = (__bf16)pv;
-          phi[s2][rb][e] = hi;
-          plo[s2][rb][e] = (__bf16)(pv - (float)hi);
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pv = {p[2 * s2 + (e >> 2)][e & 3], p[2 * s2 + (e >> 2)][(e & 3) + 1]};
+          const bf16x2 hi = __builtin_convertvector(pv, bf16x2);
+          const f32x2 rest = pv - __builtin_convertvector(hi, f32x2);
+          const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
+          phi[s2][rb][e] = hi[0];
+          phi[s2][rb][e + 1] = hi[1];
+          plo[s2][rb][e] = lo[0];
+          plo[s2][rb][e + 1] = lo[1];
         }
     }
 
     // rescale O only when some row of the wave moved its reference max (multiplying by 1 is exact)
-    if (__builtin_amdgcn_read_exec() &&
-        __ballot(alpha_rb[0] != 1.f || alpha_rb[1] != 1.f) != 0) {
+    if (__ballot(alpha_rb[0] != 1.f || alpha_rb[1] != 1.f) != 0) {
 #pragma unroll
       for (int db = 0; db < 16; ++db)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) oacc[db][rb] *= alpha_rb[rb];
     }
 
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        // source lane c16 points at key 32s2 + 4u + c16/4 (+16 for the second half), dims 16db + 4(c16%4)
-        const int d_off = (16 * db + 4 * (c16 & 3)) * 2;
+    // ---- O^T += V(t)^T P(t)^T ----
+    // step (s2, db): V^T fragment from two transpose reads, then 4 MFMAs; reads PV_AHEAD steps ahead
+    {
+      constexpr int PV_AHEAD = 3;
+      const char* vbuf = s_v[t & 1];
+      auto vfrag = [&](int st) {
+        const int s2 = st >> 4, db = st & 15;
+        // source lane c16 points at key 32s2 + 4u + c16/4 (+16 for the second half), dims
+        // 16db + 4(c16%4): chunk 2db + (c16%4)/2 of the row, half c16%2 of it
+        const int cv = 2 * db + ((c16 & 3) >> 1), hb = (c16 & 1) * 8;
         const int r1 = 32 * s2 + 4 * u + (c16 >> 2);
-        const bf16x4 v1 = lds_tr16(vbuf, r1 * V_STRIDE + d_off);
-        const bf16x4 v2 = lds_tr16(vbuf, (r1 + 16) * V_STRIDE + d_off);
-        const bf16x8 vf = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+        const bf16x4 v1 = lds_tr16(vbuf, r1 * ROWB + v_slot(r1, cv) * 16 + hb);
+        const bf16x4 v2 = lds_tr16(vbuf, (r1 + 16) * ROWB + v_slot(r1 + 16, cv) * 16 + hb);
+        return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+      };
+      bf16x8 ring[PV_AHEAD];
+#pragma unroll
+      for (int st = 0; st < PV_AHEAD; ++st) ring[st] = vfrag(st);
+#pragma unroll
+      for (int st = 0; st < 32; ++st) {
+        const bf16x8 vf = ring[st % PV_AHEAD];
+        if (st + PV_AHEAD < 32) ring[st % PV_AHEAD] = vfrag(st + PV_AHEAD);
+        const int s2 = st >> 4, db = st & 15;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[s2][rb], oacc[db][rb], 0, 0, 0);
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[s2][rb], oacc[db][rb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 0);
+#pragma unroll
+      for (int st = 0; st < 32 - PV_AHEAD; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * PV_AHEAD, 0);
     }
 
-    // ---- next tile: registers -> the other LDS buffer, then prefetch the one after ----
-    if (t + 1 < nt) {
-      store_tile(buf ^ 1);
-      if (t + 2 < nt) stage_keyat(t + 2);
-    }
+    // ---- K(t+1) and V(t+1) have landed; every wave is done with K(t) and V(t) ----
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < nt) load_tile(t + 2);
   }
 
   // ---- normalise and write: lane holds O^T[16db + 4u + i][row 16rb + c16] ----
