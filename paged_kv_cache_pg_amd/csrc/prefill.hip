@@ -129,11 +129,16 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     }
   }
 
-  // key_at of a tile: thread < 64 looks up one key (slot tt mod 2)
-  auto stage_keyat = [&](int tt) {
+  // key_at of a tile: thread < 64 looks up one key (slot tt mod 2).  The table entry is read one
+  // iteration before its offset is written, so no wave waits on a table read inside the loop.
+  auto key_page = [&](int tt) -> int32_t {
+    const int key = tt * PF_KT + tid;
+    return (tid < PF_KT && tt < nt && key < kmax) ? pg_page(a.pg, 0, key) : 0;
+  };
+  auto stage_keyat = [&](int tt, int32_t page) {
     if (tid < PF_KT && tt < nt) {
       const int key = tt * PF_KT + tid;
-      s_keyat[tt & 1][tid] = key < kmax ? pg_at(a.pg, 0, g, key, ROWB) : (int64_t)-1;
+      s_keyat[tt & 1][tid] = key < kmax ? pg_offset(a.pg, page, g, key, ROWB) : (int64_t)-1;
     }
   };
   // One tile's K and V rows, global -> LDS directly (no registers): load i of wave w fills LDS
@@ -157,13 +162,30 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
                                        16, 0, 0);
     }
   };
-  // S^T of one tile: sacc[kb][rb] holds keys 16kb + 4u + i of rows 16rb + c16.  The 32 K
-  // fragments (kb, ds) are read QK_AHEAD steps before their two MFMAs.
+  // Swizzled LDS read offsets, the same for every tile: K fragment (kb, ds) of this lane is row
+  // 16kb + c16, chunk 4ds + u -> koff[ds] + 8192 kb.  V^T half-fragment (s2, db, second half h)
+  // is row r1 = 32s2 + 4u + c16/4 + 16h, dims 16db + 4(c16%4): its slot is (2db + j) ^ 2x with
+  // j = (c16%4)/2 and x = r1 mod 8 = (4u + c16/4) mod 8, i.e. 2(db ^ x) + j, so with db = 8dh + dl
+  // the offset is voff[dl] + 256 dh + 16384 s2 + 8192 h.
+  int koff[8], voff[8];
+  {
+    const int x = (4 * u + (c16 >> 2)) & 7, j = (c16 & 3) >> 1, hb = (c16 & 1) * 8;
+    const int r0 = 4 * u + (c16 >> 2);
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) koff[ds] = c16 * ROWB + k_slot(c16, 4 * ds + u) * 16;
+#pragma unroll
+    for (int dl = 0; dl < 8; ++dl) voff[dl] = r0 * ROWB + (2 * (dl ^ x) + j) * 16 + hb;
+  }
+
+  // S^T of one tile: sacc[kb][rb] holds keys 16kb + 4u + i of rows 16rb + c16, summed over ds
+  // in order.  Steps run ds-major so that the 8 accumulators take turns (a dependent MFMA is
+  // 8 issues behind its predecessor); the K fragment of step (ds, kb) is read QK_AHEAD steps
+  // before its two MFMAs.
   auto qk = [&](const char* kbuf, f32x4 (&sacc)[4][2]) {
     constexpr int QK_AHEAD = 4;
     auto kfrag = [&](int st) {
-      const int kb = st >> 3, ds = st & 7, row = 16 * kb + c16;
-      return *(const bf16x8*)(kbuf + row * ROWB + k_slot(row, 4 * ds + u) * 16);
+      const int ds = st >> 2, kb = st & 3;
+      return *(const bf16x8*)(kbuf + koff[ds] + 16 * ROWB * kb);
     };
     bf16x8 ring[QK_AHEAD];
 #pragma unroll
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     for (int st = 0; st < 32; ++st) {
       const bf16x8 kf = ring[st % QK_AHEAD];
       if (st + QK_AHEAD < 32) ring[st % QK_AHEAD] = kfrag(st + QK_AHEAD);
-      const int kb = st >> 3, ds = st & 7;
+      const int ds = st >> 2, kb = st & 3;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
         sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sacc[kb][rb], 0, 0, 0);
@@ -199,8 +221,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
 
   // ---- prologue: K(0), V(0) into LDS ----
-  stage_keyat(0);
-  stage_keyat(1);
+  stage_keyat(0, key_page(0));
+  stage_keyat(1, key_page(1));
+  int32_t page_next = key_page(2);
   __syncthreads();
   load_tile(0, s_k[0], s_v[0]);
   __builtin_amdgcn_s_waitcnt(0);
@@ -211,7 +234,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     // K(t+1), V(t+1) into the buffers tile t-1 left; they land during this iteration and are
     // waited for at its end
     if (t + 1 < nt) load_tile(t + 1, s_k[(t + 1) & 1], s_v[(t + 1) & 1]);
-    stage_keyat(t + 2);
+    stage_keyat(t + 2, page_next);
+    page_next = key_page(t + 3);
 
     f32x4 s_cur[4][2];
     qk(s_k[t & 1], s_cur);
@@ -274,41 +298,51 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     }
 
     // ---- O^T += V(t)^T P(t)^T ----
-    // step (s2, db): V^T fragment from two transpose reads, then 4 MFMAs; reads PV_AHEAD steps ahead
+    // Step (s2, db pair): two V^T fragments (four transpose reads), then 8 MFMAs: the hi parts of
+    // both dims blocks and both row blocks, then the lo parts, so an accumulator's lo MFMA is 4
+    // issues behind its hi MFMA (each accumulator still adds hi then lo, s2 = 0 then 1).
+    // Fragments are read PV_AHEAD steps ahead.
     {
-      constexpr int PV_AHEAD = 3;
+      constexpr int PV_AHEAD = 2;
       const char* vbuf = s_v[t & 1];
-      auto vfrag = [&](int st) {
-        const int s2 = st >> 4, db = st & 15;
-        // source lane c16 points at key 32s2 + 4u + c16/4 (+16 for the second half), dims
-        // 16db + 4(c16%4): chunk 2db + (c16%4)/2 of the row, half c16%2 of it
-        const int cv = 2 * db + ((c16 & 3) >> 1), hb = (c16 & 1) * 8;
-        const int r1 = 32 * s2 + 4 * u + (c16 >> 2);
-        const bf16x4 v1 = lds_tr16(vbuf, r1 * ROWB + v_slot(r1, cv) * 16 + hb);
-        const bf16x4 v2 = lds_tr16(vbuf, (r1 + 16) * ROWB + v_slot(r1 + 16, cv) * 16 + hb);
+      auto vfrag = [&](int s2, int db) {
+        const int o = voff[db & 7] + 256 * (db >> 3) + 32 * ROWB * s2;
+        const bf16x4 v1 = lds_tr16(vbuf, o);
+        const bf16x4 v2 = lds_tr16(vbuf, o + 16 * ROWB);
         return bf16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
       };
-      bf16x8 ring[PV_AHEAD];
+      bf16x8 ring[PV_AHEAD][2];
 #pragma unroll
-      for (int st = 0; st < PV_AHEAD; ++st) ring[st] = vfrag(st);
+      for (int st = 0; st < PV_AHEAD; ++st)
 #pragma unroll
-      for (int st = 0; st < 32; ++st) {
-        const bf16x8 vf = ring[st % PV_AHEAD];
-        if (st + PV_AHEAD < 32) ring[st % PV_AHEAD] = vfrag(st + PV_AHEAD);
-        const int s2 = st >> 4, db = st & 15;
+        for (int e = 0; e < 2; ++e) ring[st][e] = vfrag(st >> 3, 2 * (st & 7) + e);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[s2][rb], oacc[db][rb], 0, 0, 0);
-          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[s2][rb], oacc[db][rb], 0, 0, 0);
+      for (int st = 0; st < 16; ++st) {
+        const int s2 = st >> 3, db0 = 2 * (st & 7);
+        bf16x8 vf[2] = {ring[st % PV_AHEAD][0], ring[st % PV_AHEAD][1]};
+        if (st + PV_AHEAD < 16) {
+          const int sn = st + PV_AHEAD;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) ring[st % PV_AHEAD][e] = vfrag(sn >> 3, 2 * (sn & 7) + e);
         }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 0);
 #pragma unroll
-      for (int st = 0; st < 32 - PV_AHEAD; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            oacc[db0 + e][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[e], phi[s2][rb], oacc[db0 + e][rb], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            oacc[db0 + e][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[e], plo[s2][rb], oacc[db0 + e][rb], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * PV_AHEAD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PV_AHEAD, 0);
+#pragma unroll
+      for (int st = 0; st < 16 - PV_AHEAD; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * PV_AHEAD, 0);
     }
 
     // ---- K(t+1) and V(t+1) have landed; every wave is done with K(t) and V(t) ----
