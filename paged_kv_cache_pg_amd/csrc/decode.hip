@@ -14,9 +14,12 @@
 // A wave processes one tile in three phases:
 //   QK:   16 lanes a key, 4 keys a step; each lane holds 16 dims of q for the G
 //         query heads of the KV group and reduces its partial dots across its
-//         16-lane row with DPP; scores go to LDS.
+//         16-lane row with permlane swaps and DPP; scores go to LDS.
 //   soft: online softmax over the tile (running max m and sum l a head).
-//   PV:   32 lanes a key, 2 keys a step; each lane accumulates G x 8 outputs.
+//   PV:   32 lanes a key, 4 keys a step; each lane accumulates G x 8 outputs.
+// The 16 K steps and 16 V steps of a tile form one sequence of loads; a ring keeps
+// the next step in flight across the softmax and across tile boundaries, so the
+// memory pipe never drains between phases or tiles.
 // Waves merge in order inside the workgroup, splits merge in order in the
 // combine kernel.  No atomics anywhere.
 #include "internal.h"
@@ -27,7 +30,7 @@ namespace {
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PAGED_DEC_RING
-#define PAGED_DEC_RING 4         // 4-key steps of K/V buffered a lane (bf16)
+#define PAGED_DEC_RING 2         // 4-key steps of K/V buffered a lane
 #endif
 #ifndef PAGED_DEC_MAX_SPLITS
 #define PAGED_DEC_MAX_SPLITS 16  // splits a stream at most
@@ -205,14 +208,13 @@ __device__ __forceinline__ int stream_keys(const DecArgs& a, int s) {
   return min(max(v, 0), a.max_len);
 }
 
-// K and V chunks a lane holds for one 4-key step: K of tile t (16 lanes a key) and
-// V of tile t-1 (32 lanes a key, two half steps).
+// One 4-key step of loads, the same register footprint for both kinds: a K step (QK, 16 lanes a
+// key) fills x[0 .. NCQ-1]; a V step (PV, 32 lanes a key, two half steps of 2 keys) fills
+// x[NCP*j .. NCP*j + NCP-1] for half step j.
 template <bool BF16>
 struct StepBuf {
   static constexpr int NCQ = (HD * (BF16 ? 2 : 4)) / 256;
-  static constexpr int NCP = (HD * (BF16 ? 2 : 4)) / 512;
-  uint4 k[NCQ];
-  uint4 v[2][NCP];
+  uint4 x[NCQ];
 };
 
 template <bool BF16, int G>
@@ -223,13 +225,15 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   constexpr int NCP = ROWB / 512;  // 16-byte chunks a lane in PV (32 lanes a key)
   constexpr int EPC = 16 / ES;     // elements a chunk
   constexpr int NO = NCP * EPC;    // outputs a lane a head (8)
-  constexpr int NSTEP = TILE / 4;  // 4-key steps a tile
-  constexpr int RING = BF16 ? PAGED_DEC_RING : 2;  // step buffers (divides NSTEP: compile-time slots)
-  constexpr int DEPTH = RING - 1;      // steps of K/V in flight ahead of the one computed
+  constexpr int NSTEP = TILE / 4;  // 4-key steps a tile and phase
+  constexpr int SPT = 2 * NSTEP;   // load steps a tile: NSTEP of K, then NSTEP of V
+  constexpr int RING = BF16 ? PAGED_DEC_RING : 2;  // step buffers (divides SPT: compile-time slots)
+  constexpr int DEPTH = RING - 1;       // steps of K/V in flight ahead of the one computed
+  static_assert(SPT % RING == 0, "ring slots must be compile-time");
   using Buf = StepBuf<BF16>;
 
   __shared__ int64_t s_keyat[NWAVE][4][TILE];
-  __shared__ float s_sc[NWAVE][2][TILE * G];
+  __shared__ float s_sc[NWAVE][TILE * G];
   __shared__ float s_alpha[NWAVE][G];
   __shared__ float s_o[NWAVE][G][HD];
   __shared__ float s_m[NWAVE][G];
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   };
   auto key_pos = [&](int tt, int id) -> int {
     const int i = (t_begin + tt) * TILE + lane;
-    if (i >= n) return -1;
+    if (i >= n || tt >= T) return -1;
     if (a.ids == nullptr) return i;
     return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
   };
@@ -271,23 +275,24 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
   const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * ROWB;
 
-  // Loads for step i of iteration tt: K rows of tile tt and V rows of tile tt-1.  Every load is
-  // issued (masked keys and missing tiles read the q row instead) so none sits under a branch.
+  // Loads of global step gs = SPT * tt + i: i < NSTEP is K step i of tile tt, else V step i - NSTEP.
+  // Every load is issued (masked keys and steps past the wave's tiles read the q row instead) so none
+  // sits under a branch.
   auto load_step = [&](int tt, int i, Buf& b) {
-    {
-      const bool ok_t = tt < T;
+    const bool ok_t = tt < T;
+    if (i < NSTEP) {
       const int64_t off = s_keyat[w][tt & 3][4 * i + grp];
       const char* kp = (ok_t && off >= 0) ? a.kb + off : qrow;
 #pragma unroll
-      for (int cc = 0; cc < NCQ; ++cc) b.k[cc] = ld_stream(kp + 256 * cc + 16 * jj);
-    }
-    const bool ok_v = tt >= 1 && tt <= T;
+      for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream(kp + 256 * cc + 16 * jj);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t off = s_keyat[w][(tt - 1) & 3][4 * i + 2 * j + half];
-      const char* vp = (ok_v && off >= 0) ? a.vb + off : qrow;
+      for (int j = 0; j < 2; ++j) {
+        const int64_t off = s_keyat[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
+        const char* vp = (ok_t && off >= 0) ? a.vb + off : qrow;
 #pragma unroll
-      for (int cc = 0; cc < NCP; ++cc) b.v[j][cc] = ld_stream(vp + 512 * cc + 16 * j32);
+        for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
+      }
     }
   };
 
@@ -316,66 +321,66 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_step(0, d, buf[d]);
 
-    for (int t = 0; t <= T; ++t) {
-      const bool do_qk = t < T, do_pv = t >= 1;
-      if (do_pv) {
-        // Online softmax over tile t-1: lane handles flat entries i*64 + lane (head lane % G).
-        wave_lds_sync();
-        float* sc = s_sc[w][(t - 1) & 1];
-        float ev[G];
-        float tmax = NEG_INF;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-          ev[i] = sc[i * 64 + lane];
-          tmax = fmaxf(tmax, ev[i]);
-        }
-        tmax = head_max<G>(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        float tsum = 0.f;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-          const float p = (ev[i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[i] - m_new);
-          sc[i * 64 + lane] = p;
-          tsum += p;
-        }
-        tsum = head_sum<G>(tsum);
-        const float alpha = (m_run == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run = l_run * alpha + tsum;
-        m_run = m_new;
-        if (lane < G) s_alpha[w][lane] = alpha;
-        wave_lds_sync();
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float al = s_alpha[w][h];
-#pragma unroll
-          for (int e = 0; e < NO; ++e) o[h][e] *= al;
-        }
-      }
-      // key_ids -> key_at for tile t+1: one table lookup a key, finished four steps later
+    for (int t = 0; t < T; ++t) {
+      // key_ids -> key_at for tile t+1: one table lookup a key, written four steps later and first
+      // needed DEPTH steps before tile t+1 starts
       const int pos1 = key_pos(t + 1, id_next);
       const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
       id_next = load_id(t + 2);
 
 #pragma unroll
-      for (int i = 0; i < NSTEP; ++i) {
-        if (i == 4 && t + 1 < T) {
+      for (int i = 0; i < SPT; ++i) {
+        if (i == 4) {
           s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, g, pos1, ROWB) : (int64_t)-1;
           wave_lds_sync();
         }
-        // prefetch step i + DEPTH (possibly the first steps of the next iteration)
+        if (i == NSTEP) {
+          // Online softmax over tile t: lane handles flat entries k*64 + lane (head lane % G).
+          wave_lds_sync();
+          float* sc = s_sc[w];
+          float ev[G];
+          float tmax = NEG_INF;
+#pragma unroll
+          for (int k = 0; k < G; ++k) {
+            ev[k] = sc[k * 64 + lane];
+            tmax = fmaxf(tmax, ev[k]);
+          }
+          tmax = head_max<G>(tmax);
+          const float m_new = fmaxf(m_run, tmax);
+          float tsum = 0.f;
+#pragma unroll
+          for (int k = 0; k < G; ++k) {
+            const float p = (ev[k] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[k] - m_new);
+            sc[k * 64 + lane] = p;
+            tsum += p;
+          }
+          tsum = head_sum<G>(tsum);
+          const float alpha = (m_run == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run = l_run * alpha + tsum;
+          m_run = m_new;
+          if (lane < G) s_alpha[w][lane] = alpha;
+          wave_lds_sync();
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float al = s_alpha[w][h];
+#pragma unroll
+            for (int e = 0; e < NO; ++e) o[h][e] *= al;
+          }
+        }
+        // prefetch global step SPT*t + i + DEPTH (possibly in the next tile)
         {
           const int ii = i + DEPTH;
-          if (ii < NSTEP) load_step(t, ii, buf[ii % RING]);
-          else load_step(t + 1, ii - NSTEP, buf[ii % RING]);
+          if (ii < SPT) load_step(t, ii, buf[ii % RING]);
+          else load_step(t + 1, ii - SPT, buf[ii % RING]);
         }
         const Buf& cur = buf[i % RING];
-        if (do_qk) {
+        if (i < NSTEP) {
           float acc[G];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float x = 0.f;
 #pragma unroll
-            for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], cur.k[cc], x);
+            for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], cur.x[cc], x);
             acc[h] = x;
           }
           using R = QkReduce<G>;
@@ -386,17 +391,19 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
             const bool valid = s_keyat[w][t & 3][kk] >= 0;
 #pragma unroll
             for (int k = 0; k < R::NR; ++k)
-              s_sc[w][t & 1][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
+              s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
           }
-        }
-        if (do_pv) {
-          const float* pp = s_sc[w][(t - 1) & 1];
+        } else {
+          const float* pp = s_sc[w];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int kk = 4 * i + 2 * j + half;
+            const int kk = 4 * (i - NSTEP) + 2 * j + half;
             float vf[NO];
+            uint4 vv[NCP];
 #pragma unroll
-            for (int cc = 0; cc < NCP; ++cc) unpack16<BF16>(cur.v[j][cc], vf + cc * EPC);
+            for (int cc = 0; cc < NCP; ++cc) vv[cc] = cur.x[NCP * j + cc];
+#pragma unroll
+            for (int cc = 0; cc < NCP; ++cc) unpack16<BF16>(vv[cc], vf + cc * EPC);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               const float p = pp[kk * G + h];
@@ -406,6 +413,8 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
           }
         }
       }
+      // every lane is done reading this tile's probabilities before the next tile's scores land
+      wave_lds_sync();
     }
   }
 
