@@ -471,34 +471,47 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   __shared__ float s_scale[MAX_SPLITS];
   __shared__ float s_L;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  const int64_t row0 = ((int64_t)s * a.hq + h) * a.ns_max;
+  // Every load is issued before any result is needed: the split count (from the stream's length),
+  // the splits' (m, l) and this thread's output dimension of every split slot.  Slots past the
+  // stream's split count hold stale values and are never used.
   const int n = stream_keys(a, s);
+  float po[MAX_SPLITS];
+#pragma unroll
+  for (int c = 0; c < MAX_SPLITS; ++c) po[c] = c < a.ns_max ? a.part_o[(row0 + c) * HD + d] : 0.f;
+  const int lc = threadIdx.x & 63;
+  float mc = NEG_INF, lv = 0.f;
+  if (threadIdx.x < 64 && lc < a.ns_max) {
+    mc = a.part_ml[(row0 + lc) * 2];
+    lv = a.part_ml[(row0 + lc) * 2 + 1];
+  }
   const int ns = dec_splits(n);
   float* outp = a.out + ((int64_t)s * a.hq + h) * HD;
   if (ns == 0) {
     outp[d] = 0.f;
     return;
   }
-  const int64_t row0 = ((int64_t)s * a.hq + h) * a.ns_max;
   if (threadIdx.x < 64) {
-    const int c = threadIdx.x;
-    const float mc = c < ns ? a.part_ml[(row0 + c) * 2] : NEG_INF;
+    if (lc >= ns) {
+      mc = NEG_INF;
+      lv = 0.f;
+    }
     float M = mc;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float sc = (mc == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    if (c < ns) s_scale[c] = sc;
-    const float lc = c < ns ? a.part_ml[(row0 + c) * 2 + 1] : 0.f;
+    if (lc < MAX_SPLITS) s_scale[lc] = sc;
     // L in split order (lane 0 walks the splits)
-    float term = sc * lc;
+    const float term = sc * lv;
     float L = 0.f;
     for (int cc = 0; cc < ns; ++cc) L += __shfl(term, cc);
-    if (c == 0) s_L = L;
+    if (lc == 0) s_L = L;
   }
   __syncthreads();
   float O = 0.f;
-  const float* po = a.part_o + row0 * HD + d;
-#pragma unroll 8
-  for (int c = 0; c < ns; ++c) O += s_scale[c] * po[(int64_t)c * HD];
+#pragma unroll
+  for (int c = 0; c < MAX_SPLITS; ++c)
+    if (c < ns) O += s_scale[c] * po[c];
   const float L = s_L;
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
