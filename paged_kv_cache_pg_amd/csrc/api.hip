@@ -261,7 +261,7 @@ int paged_block_scores_topk(const void* qi, int32_t qi_dtype, int32_t n_idx_head
   if (out_scores != nullptr && !al(out_scores, 8)) return PAGED_EINVAL;
   const int max_blocks = max_len / 4;
   const size_t need = topk_workspace_bytes(n_streams, max_blocks, k, out_scores != nullptr);
-  if (workspace_bytes < need || (need > 0 && (workspace == nullptr || !al(workspace, 16)))) return PAGED_EWORKSPACE;
+  if (workspace_bytes < need || workspace == nullptr || !al(workspace, 16)) return PAGED_EWORKSPACE;
   TopkArgs a;
   a.qi = qi;
   a.pooled = (const char*)pooled;
@@ -271,7 +271,8 @@ int paged_block_scores_topk(const void* qi, int32_t qi_dtype, int32_t n_idx_head
   a.idx_dim = idx_dim;
   a.max_blocks = max_blocks;
   a.k = k;
-  a.scores = out_scores ? out_scores : (double*)workspace;
+  a.hist = (uint32_t*)workspace;
+  a.scores = out_scores ? out_scores : (double*)((char*)workspace + (size_t)n_streams * 4096 * sizeof(uint32_t));
   a.out_ids = out_ids;
   a.out_count = out_count;
   return hip_status(launch_scores_topk(a, qi_dtype == PAGED_BF16, n_streams, stream));

@@ -71,6 +71,7 @@ struct TopkArgs {
   int32_t max_blocks;     // max_len / 4
   int32_t k;
   double* scores;         // [S][max_blocks]
+  uint32_t* hist;         // workspace [S][4096]: coarse score histograms
   int32_t* out_ids;       // [S][k]
   int32_t* out_count;     // [S]
 };

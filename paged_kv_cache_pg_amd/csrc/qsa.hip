@@ -78,6 +78,13 @@ constexpr int SC_NB = 64;                 // blocks a workgroup
 constexpr int SC_DCH = 128;               // dims a staged chunk (generic kernel)
 constexpr int SC_ROWB = SC_DCH * 4 + 16;  // LDS bytes a staged row (pad: consecutive rows 4 banks apart)
 
+// The first workgroup of each stream clears the stream's coarse top-k histogram (the
+// histogram kernel, launched next on the same stream, adds into it).
+__device__ __forceinline__ void zero_hist(const TopkArgs& a, int s) {
+  uint4* h = (uint4*)(a.hist + (int64_t)s * 4096);
+  for (int i = threadIdx.x; i < 4096 / 4; i += SC_NB) h[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 template <bool QBF16>
 __device__ __forceinline__ void widen_q(const TopkArgs& a, int s, double* s_q) {
   const int m = a.n_idx_heads * a.idx_dim;
@@ -97,6 +104,7 @@ __global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x 128], dynamic
   __shared__ int64_t s_base[SC_NB];
   const int s = blockIdx.y, lane = threadIdx.x;
+  if (blockIdx.x == 0) zero_hist(a, s);
   const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
   const int b0 = blockIdx.x * SC_NB;
   if (b0 >= nb) return;
@@ -164,6 +172,7 @@ __global__ __launch_bounds__(SC_NB) void scores_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x dims], dynamic
   __shared__ int64_t s_base[SC_NB];
   const int s = blockIdx.y, lane = threadIdx.x;
+  if (blockIdx.x == 0) zero_hist(a, s);
   const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
   const int b0 = blockIdx.x * SC_NB;
   if (b0 >= nb) return;
@@ -205,26 +214,34 @@ __global__ __launch_bounds__(SC_NB) void scores_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one workgroup a stream, item i = j * 1024 + thread for chunk j (so
-// every read is coalesced and item order is (chunk, thread) = id order).
-//  1. Coarse pass: a 4096-bin histogram of the top 12 bits of the float32
-//     order key (sign, exponent, 3 mantissa bits).  Rounding to float32 is
-//     monotone, so every item in a higher bin has a higher score; the bin T
-//     where the count from the top reaches k holds the k-th largest score.
-//  2. Refinement inside bin T on the exact 64-bit order keys: skip the bits all
-//     candidates share (from their min and max), then 8-bit digits, until the
-//     chosen digit holds exactly the keys still needed or all 64 bits are fixed.
-//  3. Compaction in id order: everything above the threshold, plus the first
-//     krem items (lowest ids) equal to it.  Ids come out ascending.
-// With at most 32 chunks the scores are read once: chunks 0-15 stay in registers,
-// chunks 16-31 in LDS.
+// Top-k, three steps (the block order a score sorts by: score descending, then
+// id ascending; -0.0 == +0.0):
+//  1. Coarse histogram (hist_kernel, many workgroups a stream): 4096 bins of the
+//     top 12 bits of the float32 order key of each score (sign, exponent, 3
+//     mantissa bits).  Rounding to float32 is monotone, so every score in a
+//     higher bin is larger than every score in a lower one.  The scores kernel
+//     zeroes the histogram; this kernel adds each workgroup's LDS histogram to it.
+//  2. Selection (topk_kernel, one workgroup a stream): the bin T where the count
+//     from the top reaches k holds the k-th block; krem blocks are still needed
+//     from it.  One sweep over the scores appends the ids of higher bins to an
+//     LDS list and bin T's (key, id) pairs to a candidate list; each candidate is
+//     ranked exactly (candidates ahead of it in the sort order, counted a wave at
+//     a time) and the krem of rank < krem join the list.
+//  3. Order: each listed id's place is the number of listed ids below it.
+// With more than TK_CMAX candidates (heavy ties) or k > TK_AMAX, a radix
+// refinement on the exact 64-bit keys of bin T finds the threshold instead (ties
+// at it go to the lowest ids), and a count sweep, a 16-entry scan of the waves'
+// counts and a write sweep compact the ids in order (wave w holds ids
+// [64 J w, 64 J (w+1))).
 // ---------------------------------------------------------------------------
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_KREG = 16;         // chunks kept in registers
-constexpr int TK_KLDS = 16;         // chunks kept in LDS (with the registers: 32768 blocks)
 constexpr int TK_BINS = 4096;       // coarse bins
-constexpr int TK_SUPER = 64;        // chunks a compaction round
+constexpr int TK_CMAX = 4096;       // candidates ranked in LDS
+constexpr int TK_AMAX = 8192;       // k at most for the list path
+constexpr int TK_BATCH = 16;        // score chunks a thread reads at once
+constexpr int HK_ITEMS = 1024;      // scores a histogram workgroup
+constexpr int HK_THREADS = 256;
 
 __device__ __forceinline__ uint64_t order_key(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
@@ -286,20 +303,55 @@ __device__ __forceinline__ uint64_t wg_scan64(uint64_t v, uint64_t* s_tmp, uint6
   return r;
 }
 
-template <bool REG>
+__device__ __forceinline__ int stream_blocks(const TopkArgs& a, int s) {
+  return min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+}
+
+// Step 1: each workgroup histograms HK_ITEMS scores of one stream in LDS and adds the
+// non-zero bins to the stream's histogram (zeroed by the scores kernel).
+__global__ __launch_bounds__(HK_THREADS) void hist_kernel(TopkArgs a) {
+  __shared__ uint32_t s_h[TK_BINS];
+  const int s = blockIdx.y;
+  const int nb = stream_blocks(a, s);
+  const int i0 = blockIdx.x * HK_ITEMS;
+  if (nb <= a.k || i0 >= nb) return;  // nothing to select, or past the stream's blocks
+  for (int i = threadIdx.x; i < TK_BINS; i += HK_THREADS) s_h[i] = 0;
+  const double* sc = a.scores + (int64_t)s * a.max_blocks;
+  double x[HK_ITEMS / HK_THREADS];
+#pragma unroll
+  for (int r = 0; r < HK_ITEMS / HK_THREADS; ++r) {
+    const int i = i0 + r * HK_THREADS + threadIdx.x;
+    x[r] = i < nb ? sc[i] : 0.0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < HK_ITEMS / HK_THREADS; ++r) {
+    const int i = i0 + r * HK_THREADS + threadIdx.x;
+    if (i < nb) lds_count(s_h, coarse_bin(x[r]));
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (int64_t)s * TK_BINS;
+  for (int b = threadIdx.x; b < TK_BINS; b += HK_THREADS) {
+    const uint32_t c = s_h[b];
+    if (c) atomicAdd(&gh[b], c);
+  }
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t s_hist[TK_BINS];
-  __shared__ uint32_t s_cnt[2][TK_SUPER][TK_WAVES];
+  __shared__ int32_t s_aid[TK_AMAX];   // ids taken (unordered until the final ranking)
+  __shared__ uint64_t s_ckey[TK_CMAX]; // candidates of bin T: exact keys and ids
+  __shared__ int32_t s_cid[TK_CMAX];
+  __shared__ uint32_t s_dig[256];
   __shared__ uint64_t s_tmp[TK_WAVES + 1];
   __shared__ uint64_t s_red[2][TK_WAVES];
-  __shared__ uint32_t s_T;
+  __shared__ uint32_t s_wg[TK_WAVES], s_we[TK_WAVES];
+  __shared__ uint32_t s_T, s_na, s_nc;
   __shared__ int s_krem, s_done;
   __shared__ uint64_t s_prefix;
-  __shared__ double s_keys[REG ? TK_KLDS : 1][TK_THREADS];
 
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+  const int nb = stream_blocks(a, s);
   const int k = a.k;
   int32_t* ids = a.out_ids + (int64_t)s * k;
   const double* sc = a.scores + (int64_t)s * a.max_blocks;
@@ -309,67 +361,39 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     if (tid == 0) a.out_count[s] = nb;
     return;
   }
-  const int J = (nb + TK_THREADS - 1) / TK_THREADS;  // chunks
-
-  double reg[REG ? TK_KREG : 1];
-  if constexpr (REG) {
-#pragma unroll
-    for (int j = 0; j < TK_KREG; ++j) {
-      const int i = j * TK_THREADS + tid;
-      reg[j] = (j < J && i < nb) ? sc[i] : 0.0;
-    }
-    double t[TK_KLDS];
-#pragma unroll
-    for (int j = 0; j < TK_KLDS; ++j) {
-      const int i = (TK_KREG + j) * TK_THREADS + tid;
-      t[j] = (TK_KREG + j < J && i < nb) ? sc[i] : 0.0;
-    }
-#pragma unroll
-    for (int j = 0; j < TK_KLDS; ++j) s_keys[j][tid] = t[j];
-  }
-  // f(j, i, x) for every item of this thread, chunk by chunk (LDS chunks are only this thread's own)
+  const int J = (nb + TK_THREADS - 1) / TK_THREADS;  // chunks a wave
+  // item (w, j, lane) has id (w * J + j) * 64 + lane: a wave's ids are consecutive.  f(j, i, x) for every
+  // item of this thread in chunk (= id) order, TK_BATCH chunks' reads in flight at a time; items past
+  // the stream's blocks read as -inf and carry i >= nb.
+  auto item_id = [&](int j) { return (w * J + j) * 64 + lane; };
   auto for_items = [&](auto&& f) {
-    if constexpr (REG) {
+    for (int j8 = 0; j8 < J; j8 += TK_BATCH) {
+      double t[TK_BATCH];
 #pragma unroll
-      for (int j = 0; j < TK_KREG; ++j) {
-        const int i = j * TK_THREADS + tid;
-        if (j < J && i < nb) f(j, i, reg[j]);
+      for (int u = 0; u < TK_BATCH; ++u) {
+        const int i = item_id(j8 + u);
+        t[u] = (j8 + u < J && i < nb) ? sc[i] : (double)NEG_INF;
       }
-      for (int j = TK_KREG; j < J; ++j) {
-        const int i = j * TK_THREADS + tid;
-        if (i < nb) f(j, i, s_keys[j - TK_KREG][tid]);
-      }
-    } else {
-      // eight chunks' reads in flight at a time
-      for (int j8 = 0; j8 < J; j8 += 8) {
-        double t[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = (j8 + u) * TK_THREADS + tid;
-          t[u] = (j8 + u < J && i < nb) ? sc[i] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = (j8 + u) * TK_THREADS + tid;
-          if (j8 + u < J && i < nb) f(j8 + u, i, t[u]);
-        }
-      }
+      for (int u = 0; u < TK_BATCH; ++u)
+        if (j8 + u < J) f(j8 + u, item_id(j8 + u), t[u]);
     }
   };
 
-  // ---- 1. coarse histogram and the bin of the k-th largest ----
-  for (int i = tid; i < TK_BINS; i += TK_THREADS) s_hist[i] = 0;
-  __syncthreads();
-  for_items([&](int, int, double x) { lds_count(s_hist, coarse_bin(x)); });
-  __syncthreads();
+  // ---- 2. the bin of the k-th block, from the coarse histogram ----
+  if (tid == 0) {
+    s_na = 0;
+    s_nc = 0;
+  }
   {
     // thread t owns bins 4095-4t .. 4092-4t (descending)
+    const uint32_t* gh = a.hist + (int64_t)s * TK_BINS;
     const int top = TK_BINS - 1 - 4 * tid;
     uint32_t c4[4];
     uint64_t loc = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      c4[r] = s_hist[top - r];
+      c4[r] = gh[top - r];
       loc += c4[r];
     }
     uint64_t tot;
@@ -389,13 +413,63 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   }
   const uint32_t T = s_T;
   int krem = s_krem;
-  uint64_t prefix = 0, mask = 0;
 
-  // ---- 2. refinement inside bin T on the exact keys ----
-  if ((int)s_hist[T] != krem) {
+  // ---- one sweep: ids above bin T are taken; bin T's scores become candidates ----
+  const bool lists_fit = k <= TK_AMAX;
+  for_items([&](int, int i, double x) {
+    const uint32_t cb = coarse_bin(x);
+    if (i < nb && cb >= T) {
+      if (cb > T) {
+        const uint32_t slot = atomicAdd(&s_na, 1u);
+        if (slot < TK_AMAX) s_aid[slot] = i;
+      } else {
+        const uint32_t slot = atomicAdd(&s_nc, 1u);
+        if (slot < TK_CMAX) {
+          s_ckey[slot] = order_key(x);
+          s_cid[slot] = i;
+        }
+      }
+    }
+  });
+  __syncthreads();
+  const int nc = (int)s_nc;
+
+  if (lists_fit && nc <= TK_CMAX) {
+    // Exact rank of each candidate: the number of candidates ahead of it in the sort order,
+    // counted by its own thread over broadcast LDS reads; the krem of rank < krem are taken.
+    for (int c = tid; c < nc; c += TK_THREADS) {
+      const uint64_t kc = s_ckey[c];
+      const int32_t ic = s_cid[c];
+      int r = 0;
+#pragma unroll 8
+      for (int o = 0; o < nc; ++o) {
+        const uint64_t ko = s_ckey[o];
+        const int32_t io = s_cid[o];
+        r += (int)((ko > kc) | ((ko == kc) & (io < ic)));
+      }
+      if (r < krem) s_aid[atomicAdd(&s_na, 1u)] = ic;
+    }
+    __syncthreads();
+    // the k taken ids, ascending: an id's place is the number of taken ids below it
+    for (int e = tid; e < k; e += TK_THREADS) {
+      const int32_t ie = s_aid[e];
+      int r = 0;
+#pragma unroll 8
+      for (int o = 0; o < k; ++o) r += (int)(s_aid[o] < ie);
+      ids[r] = ie;
+    }
+    if (tid == 0) a.out_count[s] = k;
+    return;
+  }
+
+  // ---- fallback (more than TK_CMAX candidates or k > TK_AMAX): radix refinement inside bin T ----
+  // Skip the bits all candidates share, then 8-bit digits until the chosen digit holds exactly the
+  // keys still needed or all bits are fixed; ties at the threshold go to the lowest ids.
+  uint64_t prefix = 0, mask = 0;
+  {
     uint64_t kmin = ~0ull, kmax = 0;
-    for_items([&](int, int, double x) {
-      if (coarse_bin(x) == T) {
+    for_items([&](int, int i, double x) {
+      if (i < nb && coarse_bin(x) == T) {
         const uint64_t ok = order_key(x);
         kmin = ok < kmin ? ok : kmin;
         kmax = ok > kmax ? ok : kmax;
@@ -430,12 +504,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         const int nd = hb - lo + 1;
         const uint64_t dmask = ((1ull << nd) - 1) << lo;
         __syncthreads();
-        for (int i = tid; i < 256; i += TK_THREADS) s_hist[i] = 0;
+        for (int i = tid; i < 256; i += TK_THREADS) s_dig[i] = 0;
         __syncthreads();
-        for_items([&](int, int, double x) {
-          if (coarse_bin(x) == T) {
+        for_items([&](int, int i, double x) {
+          if (i < nb && coarse_bin(x) == T) {
             const uint64_t ok = order_key(x);
-            if ((ok & mask) == prefix) lds_count(s_hist, (uint32_t)((ok & dmask) >> lo));
+            if ((ok & mask) == prefix) lds_count(s_dig, (uint32_t)((ok & dmask) >> lo));
           }
         });
         __syncthreads();
@@ -446,7 +520,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int d = 255 - 4 * lane - r;
-            c4[r] = d < (1 << nd) ? s_hist[d] : 0u;
+            c4[r] = d < (1 << nd) ? s_dig[d] : 0u;
             loc += c4[r];
           }
           uint32_t incl = loc;
@@ -480,53 +554,55 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
       }
     }
   }
-
-  // ---- 3. compaction in id order ----
-  // gt: above the threshold; eq: equal to it (the first krem of them, by id, are taken)
-  auto classify = [&](double x, bool& gt, bool& eq) {
+  // gt: taken for certain; eq: tied at the threshold (the first krem of them by id are taken)
+  auto classify = [&](int i, double x, bool& gt, bool& eq) {
     const uint32_t cb = coarse_bin(x);
-    const uint64_t ok = order_key(x) & mask;
-    gt = cb > T || (cb == T && ok > prefix);
-    eq = cb == T && ok == prefix;
+    const uint64_t om = order_key(x) & mask;
+    gt = (i < nb) & ((cb > T) | ((cb == T) & (om > prefix)));
+    eq = (i < nb) & (cb == T) & (om == prefix);
   };
-  uint32_t carry_g = 0, carry_e = 0;
-  for (int j0 = 0; j0 < J; j0 += TK_SUPER) {
-    const int jn = min(TK_SUPER, J - j0);
-    for (int i = tid; i < 2 * TK_SUPER * TK_WAVES; i += TK_THREADS) (&s_cnt[0][0][0])[i] = 0;
-    __syncthreads();
-    for_items([&](int j, int, double x) {
-      if (j < j0 || j >= j0 + jn) return;
+  // compaction in id order: a count sweep, a 16-entry scan of the waves' counts, a write sweep
+  {
+    uint32_t ng = 0, ne = 0;
+    for_items([&](int, int i, double x) {
       bool gt, eq;
-      classify(x, gt, eq);
-      const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      if (lane == (int)__builtin_ctzll(__ballot(1))) {
-        s_cnt[0][j - j0][w] = (uint32_t)__popcll(mg);
-        s_cnt[1][j - j0][w] = (uint32_t)__popcll(me);
-      }
+      classify(i, x, gt, eq);
+      ng += (uint32_t)__popcll(__ballot(gt));
+      ne += (uint32_t)__popcll(__ballot(eq));
     });
-    __syncthreads();
-    {
-      // table entry (chunk jj, wave ww) = thread jj * 16 + ww, in id order
-      const int jj = tid / TK_WAVES, ww = tid % TK_WAVES;
-      const uint64_t v = (uint64_t)s_cnt[0][jj][ww] | ((uint64_t)s_cnt[1][jj][ww] << 32);
-      uint64_t tot;
-      const uint64_t ex = wg_scan64(v, s_tmp, &tot);
-      s_cnt[0][jj][ww] = carry_g + (uint32_t)ex;
-      s_cnt[1][jj][ww] = carry_e + (uint32_t)(ex >> 32);
-      carry_g += (uint32_t)tot;
-      carry_e += (uint32_t)(tot >> 32);
+    if (lane == 0) {
+      s_wg[w] = ng;
+      s_we[w] = ne;
     }
     __syncthreads();
-    for_items([&](int j, int i, double x) {
-      if (j < j0 || j >= j0 + jn) return;
-      bool gt, eq;
-      classify(x, gt, eq);
-      const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      const uint32_t eb = s_cnt[1][j - j0][w] + lanes_below(me);
-      const uint32_t pos = s_cnt[0][j - j0][w] + lanes_below(mg) + min(eb, (uint32_t)krem);
-      if ((gt || (eq && eb < (uint32_t)krem)) && pos < (uint32_t)k) ids[pos] = i;
-    });
+    if (tid < 64) {
+      uint32_t g = lane < TK_WAVES ? s_wg[lane] : 0u, e = lane < TK_WAVES ? s_we[lane] : 0u;
+      uint32_t gi = g, ei = e;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(gi, off), z = __shfl_up(ei, off);
+        if (lane >= off) {
+          gi += y;
+          ei += z;
+        }
+      }
+      if (lane < TK_WAVES) {
+        s_wg[lane] = gi - g;
+        s_we[lane] = ei - e;
+      }
+    }
     __syncthreads();
+    uint32_t run_g = s_wg[w], run_e = s_we[w];
+    for_items([&](int, int i, double x) {
+      bool gt, eq;
+      classify(i, x, gt, eq);
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t eb = run_e + lanes_below(me);
+      const uint32_t pos = run_g + lanes_below(mg) + min(eb, (uint32_t)krem);
+      if ((gt || (eq && eb < (uint32_t)krem)) && pos < (uint32_t)k) ids[pos] = i;
+      run_g += (uint32_t)__popcll(mg);
+      run_e += (uint32_t)__popcll(me);
+    });
   }
   if (tid == 0) a.out_count[s] = k;
 }
@@ -547,8 +623,9 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t st) {
 
 size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_external) {
   (void)k;
-  if (scores_external) return 0;
-  return (size_t)n_streams * (size_t)max_blocks * sizeof(double);
+  size_t b = (size_t)n_streams * TK_BINS * sizeof(uint32_t);  // coarse histograms
+  if (!scores_external) b += (size_t)n_streams * (size_t)max_blocks * sizeof(double);
+  return b;
 }
 
 hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hipStream_t st) {
@@ -567,10 +644,13 @@ hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.max_blocks <= (TK_KREG + TK_KLDS) * TK_THREADS)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
+  if (a.max_blocks > 0) {
+    dim3 grid((a.max_blocks + HK_ITEMS - 1) / HK_ITEMS, n_streams);
+    hipLaunchKernelGGL(hist_kernel, grid, dim3(HK_THREADS), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3(n_streams), dim3(TK_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
