@@ -18,7 +18,7 @@
 //   soft: online softmax over the tile (running max m and sum l a head).
 //   PV:   32 lanes a key, 4 keys a step; each lane accumulates G x 8 outputs.
 // The 16 K steps and 16 V steps of a tile form one sequence of loads; a ring keeps
-// the next step in flight across the softmax and across tile boundaries, so the
+// the next steps in flight across the softmax and across tile boundaries, so the
 // memory pipe never drains between phases or tiles.
 // Waves merge in order inside the workgroup, splits merge in order in the
 // combine kernel.  No atomics anywhere.
@@ -31,6 +31,9 @@ namespace {
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PAGED_DEC_RING
 #define PAGED_DEC_RING 2         // 4-key steps of K/V buffered a lane
+#endif
+#ifndef PAGED_DEC_RING_SHORT
+#define PAGED_DEC_RING_SHORT 4   // the same for streams of at most two tiles a wave
 #endif
 #ifndef PAGED_DEC_MAX_SPLITS
 #define PAGED_DEC_MAX_SPLITS 16  // splits a stream at most
@@ -217,7 +220,7 @@ struct StepBuf {
   uint4 x[NCQ];
 };
 
-template <bool BF16, int G>
+template <bool BF16, int G, int RING>
 __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(DecArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int ROWB = HD * ES;    // bytes a row
@@ -227,7 +230,6 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   constexpr int NO = NCP * EPC;    // outputs a lane a head (8)
   constexpr int NSTEP = TILE / 4;  // 4-key steps a tile and phase
   constexpr int SPT = 2 * NSTEP;   // load steps a tile: NSTEP of K, then NSTEP of V
-  constexpr int RING = BF16 ? PAGED_DEC_RING : 2;  // step buffers (divides SPT: compile-time slots)
   constexpr int DEPTH = RING - 1;       // steps of K/V in flight ahead of the one computed
   static_assert(SPT % RING == 0, "ring slots must be compile-time");
   using Buf = StepBuf<BF16>;
@@ -516,10 +518,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
 
+// Ring depth: one step ahead keeps the register file small for long streams, where every wave has
+// several tiles and two waves share a SIMD; streams of at most two tiles a wave (short or sparse
+// key lists) run their few steps three ahead instead.  The depth changes only when loads are
+// issued, never the arithmetic, so results do not depend on it.
 template <bool BF16, int G>
 hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv, n_streams);
-  hipLaunchKernelGGL((decode_split_kernel<BF16, G>), grid, dim3(WGS), 0, st, a);
+  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
+  const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
+  if constexpr (BF16) {
+    if (short_keys)
+      hipLaunchKernelGGL((decode_split_kernel<true, G, PAGED_DEC_RING_SHORT>), grid, dim3(WGS), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<true, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<false, G, 2>), grid, dim3(WGS), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq, n_streams), dim3(256), 0, st, a);
