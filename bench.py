@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_552_704
-DECODE_TRAFFIC_SOURCES = "5e3f1db557c9e25d"
+DECODE_TRAFFIC_BYTES = 676_355_198
+DECODE_TRAFFIC_SOURCES = "40e3b6e65999d665"
 
 
 def _decode_sources_hash() -> str:
