@@ -70,7 +70,8 @@ enum {
   PAGED_EINVAL = -1,       /* an argument is out of range, NULL or misaligned  */
   PAGED_EUNSUPPORTED = -2, /* a valid request this build does not serve        */
   PAGED_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
-  PAGED_EHIP = -4          /* a HIP launch failed                               */
+  PAGED_EHIP = -4,         /* a HIP launch failed                               */
+  PAGED_EFULL = -5         /* no free page or run: the request waits (page pool) */
 };
 
 /* The pages' Pg argument ([P1 "What this changes"]). */
@@ -233,6 +234,36 @@ int paged_rows_gather(void *dst, int64_t stride_s, int64_t stride_h, int64_t str
 int paged_row_offsets(const paged_pg *pg, int32_t n_streams, int32_t row_width,
                       const int32_t *streams, const int32_t *heads, const int32_t *positions,
                       int64_t *out, int32_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host page pool ([P2 commit 1ac2075]: the free stack hands out KV pages from
+ * the bottom; findRun / claimRun / releaseRun take k consecutive free pages
+ * from the top; a pool too fragmented for a run makes the request wait.
+ * [P2 description]: a lane's pages and run go back once the engine's stream
+ * drains -- the caller's duty; nothing here touches the GPU).
+ *
+ * The pool lives in host memory the caller owns and passes to every call:
+ * paged_pool_state_bytes(n_pages) bytes, 8-byte aligned, set up by
+ * paged_pool_init.  Calls on one state must not run concurrently.
+ *   init         all n_pages free; the stack hands out page 0 first, then 1, 2, ...
+ *   alloc        n pages off the free stack into pages[0..n-1] (in the order taken);
+ *                PAGED_EFULL (nothing taken) when fewer than n are free
+ *   free         pages handed out by alloc go back onto the stack in list order (the
+ *                last listed is handed out next); PAGED_EINVAL, with nothing changed,
+ *                for a page not handed out by alloc or listed twice
+ *   claim_run    the highest k consecutive free pages (*first = the lowest of them),
+ *                taken off the free stack; PAGED_EFULL when no such run exists
+ *   release_run  a claimed run's pages go back onto the stack, its lowest page on top;
+ *                PAGED_EINVAL unless every page of [first, first+k) belongs to a run
+ *   free_count   pages on the free stack (negative status for a bad state)
+ */
+size_t  paged_pool_state_bytes(int32_t n_pages);
+int     paged_pool_init(void *state, size_t state_size, int32_t n_pages);
+int     paged_pool_alloc(void *state, int32_t n, int32_t *pages);
+int     paged_pool_free(void *state, const int32_t *pages, int32_t n);
+int     paged_pool_claim_run(void *state, int32_t k, int32_t *first);
+int     paged_pool_release_run(void *state, int32_t first, int32_t k);
+int32_t paged_pool_free_count(const void *state);
 
 /* Text for a status code (static storage). */
 const char *paged_strerror(int status);

@@ -5,6 +5,8 @@ declared in include/paged_attn.h); ``binding`` marshals arguments to it.
 """
 from .binding import (  # noqa: F401
     PAGED_BF16,
+    PAGED_EFULL,
+    PAGED_OK,
     PAGED_F32,
     PagedError,
     make_kv,
@@ -14,7 +16,14 @@ from .binding import (  # noqa: F401
     paged_attn_prefill,
     paged_attn_prefill_workspace,
     paged_block_scores_topk,
+    paged_pool_alloc,
     paged_pool_blocks,
+    paged_pool_claim_run,
+    paged_pool_free,
+    paged_pool_free_count,
+    paged_pool_init,
+    paged_pool_release_run,
+    paged_pool_state_bytes,
     paged_row_offsets,
     paged_rows_gather,
     paged_rows_store,

@@ -26,6 +26,7 @@ PAGED_EINVAL = -1
 PAGED_EUNSUPPORTED = -2
 PAGED_EWORKSPACE = -3
 PAGED_EHIP = -4
+PAGED_EFULL = -5
 
 
 class PagedError(RuntimeError):
@@ -70,6 +71,13 @@ _SIGS = {
     "paged_row_offsets": (c_int32, [POINTER(PgStruct), c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_void_p]),
     "paged_strerror": (ctypes.c_char_p, [c_int32]),
+    "paged_pool_state_bytes": (c_size_t, [c_int32]),
+    "paged_pool_init": (c_int32, [c_void_p, c_size_t, c_int32]),
+    "paged_pool_alloc": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "paged_pool_free": (c_int32, [c_void_p, c_void_p, c_int32]),
+    "paged_pool_claim_run": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "paged_pool_release_run": (c_int32, [c_void_p, c_int32, c_int32]),
+    "paged_pool_free_count": (c_int32, [c_void_p]),
 }
 
 
@@ -207,3 +215,55 @@ def paged_row_offsets(pg: PgStruct, n_streams: int, row_width: int, streams, hea
                       stream=None):
     _check(lib().paged_row_offsets(ctypes.byref(pg), n_streams, row_width, _p(streams), _p(heads), _p(positions),
                                    _p(out), n, _stream(stream)), "paged_row_offsets")
+
+
+# ---------------------------------------------------------------------------
+# Host page pool (state in a caller-owned host buffer, e.g. a numpy uint8 array)
+# ---------------------------------------------------------------------------
+
+def _host(a) -> int:
+    """Address of a host numpy array (or an int address)."""
+    if isinstance(a, int):
+        return a
+    return a.ctypes.data
+
+
+def paged_pool_state_bytes(n_pages: int) -> int:
+    return int(lib().paged_pool_state_bytes(n_pages))
+
+
+def paged_pool_init(state, n_pages: int) -> None:
+    _check(lib().paged_pool_init(_host(state), state.nbytes, n_pages), "paged_pool_init")
+
+
+def paged_pool_alloc(state, n: int, pages) -> int:
+    """Pages into the int32 array `pages`; returns the status (PAGED_EFULL: nothing taken)."""
+    st = int(lib().paged_pool_alloc(_host(state), n, _host(pages)))
+    if st not in (PAGED_OK, PAGED_EFULL):
+        _check(st, "paged_pool_alloc")
+    return st
+
+
+def paged_pool_free(state, pages, n: int) -> None:
+    _check(lib().paged_pool_free(_host(state), _host(pages), n), "paged_pool_free")
+
+
+def paged_pool_claim_run(state, k: int) -> int:
+    """First page of the claimed run, or PAGED_EFULL when no run of k free pages exists."""
+    first = ctypes.c_int32(-1)
+    st = int(lib().paged_pool_claim_run(_host(state), k, ctypes.addressof(first)))
+    if st == PAGED_EFULL:
+        return st
+    _check(st, "paged_pool_claim_run")
+    return int(first.value)
+
+
+def paged_pool_release_run(state, first: int, k: int) -> None:
+    _check(lib().paged_pool_release_run(_host(state), first, k), "paged_pool_release_run")
+
+
+def paged_pool_free_count(state) -> int:
+    n = int(lib().paged_pool_free_count(_host(state)))
+    if n < 0:
+        _check(n, "paged_pool_free_count")
+    return n

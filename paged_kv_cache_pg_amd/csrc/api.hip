@@ -324,6 +324,7 @@ const char* paged_strerror(int status) {
     case PAGED_EUNSUPPORTED: return "unsupported by this build";
     case PAGED_EWORKSPACE: return "workspace missing or too small";
     case PAGED_EHIP: return "HIP launch failed";
+    case PAGED_EFULL: return "no free page or run (the request waits)";
     default: return "unknown status";
   }
 }

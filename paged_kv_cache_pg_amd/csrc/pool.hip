@@ -1,0 +1,154 @@
+// Host page pool for a KV arena: hands out pages for the page tables and runs of consecutive
+// pages, in the caller's memory (no allocation, no global state).
+//
+// TensorFold PR #1170, commit 1ac2075 ("a pool lane's recurrent state is a run of pool pages"):
+// the free stack hands out KV pages from the bottom; findRun / claimRun / releaseRun take k
+// consecutive free pages from the top; a pool too fragmented for a run makes the request wait.
+// Description of PR #1170: a lane's pages and run go back once the engine's stream drains (the
+// caller's duty: nothing here touches the GPU).
+//
+// State (host memory the caller owns, paged_pool_state_bytes(n) bytes):
+//   header | stack[n] int32 (free page ids; the top of the stack is stack[n_free-1]) | kind[n] uint8
+// kind: 0 free, 1 handed out as a page, 2 part of a run (3 marks a page while a free list is checked).
+#include <stdint.h>
+#include <string.h>
+
+#include "paged_attn.h"
+
+namespace {
+
+constexpr uint32_t POOL_MAGIC = 0x4c504750u;  // "PGPL"
+
+struct PoolHeader {
+  uint32_t magic;
+  int32_t n_pages;
+  int32_t n_free;
+  int32_t reserved;
+};
+
+enum : uint8_t { KIND_FREE = 0, KIND_PAGE = 1, KIND_RUN = 2, KIND_MARK = 3 };
+
+size_t state_bytes(int64_t n) {
+  const size_t b = sizeof(PoolHeader) + (size_t)n * sizeof(int32_t) + (size_t)n;
+  return (b + 7) & ~(size_t)7;
+}
+
+struct View {
+  PoolHeader* h;
+  int32_t* stack;
+  uint8_t* kind;
+};
+
+bool view_of(void* state, View* v) {
+  if (state == nullptr || ((uintptr_t)state & 7) != 0) return false;
+  PoolHeader* h = (PoolHeader*)state;
+  if (h->magic != POOL_MAGIC || h->n_pages < 1 || h->n_free < 0 || h->n_free > h->n_pages) return false;
+  v->h = h;
+  v->stack = (int32_t*)(h + 1);
+  v->kind = (uint8_t*)(v->stack + h->n_pages);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_pool_state_bytes(int32_t n_pages) {
+  if (n_pages < 1) return 0;
+  return state_bytes(n_pages);
+}
+
+int paged_pool_init(void* state, size_t state_size, int32_t n_pages) {
+  if (state == nullptr || ((uintptr_t)state & 7) != 0 || n_pages < 1) return PAGED_EINVAL;
+  if (state_size < state_bytes(n_pages)) return PAGED_EWORKSPACE;
+  PoolHeader* h = (PoolHeader*)state;
+  h->magic = POOL_MAGIC;
+  h->n_pages = n_pages;
+  h->n_free = n_pages;
+  h->reserved = 0;
+  int32_t* stack = (int32_t*)(h + 1);
+  uint8_t* kind = (uint8_t*)(stack + n_pages);
+  // page 0 on top: pages come off the stack from the bottom of the arena up
+  for (int32_t i = 0; i < n_pages; ++i) stack[i] = n_pages - 1 - i;
+  memset(kind, KIND_FREE, (size_t)n_pages);
+  return PAGED_OK;
+}
+
+int32_t paged_pool_free_count(const void* state) {
+  View v;
+  if (!view_of((void*)state, &v)) return PAGED_EINVAL;
+  return v.h->n_free;
+}
+
+int paged_pool_alloc(void* state, int32_t n, int32_t* pages) {
+  View v;
+  if (!view_of(state, &v) || n < 0 || (n > 0 && pages == nullptr)) return PAGED_EINVAL;
+  if (n > v.h->n_free) return PAGED_EFULL;  // nothing is taken: the request waits
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t p = v.stack[--v.h->n_free];
+    v.kind[p] = KIND_PAGE;
+    pages[i] = p;
+  }
+  return PAGED_OK;
+}
+
+int paged_pool_free(void* state, const int32_t* pages, int32_t n) {
+  View v;
+  if (!view_of(state, &v) || n < 0 || (n > 0 && pages == nullptr)) return PAGED_EINVAL;
+  // every page must be one handed out as a page, each at most once; nothing changes otherwise
+  int32_t i = 0;
+  for (; i < n; ++i) {
+    const int32_t p = pages[i];
+    if (p < 0 || p >= v.h->n_pages || v.kind[p] != KIND_PAGE) break;
+    v.kind[p] = KIND_MARK;  // a page listed twice meets its mark
+  }
+  if (i < n) {
+    for (int32_t j = 0; j < i; ++j) v.kind[pages[j]] = KIND_PAGE;
+    return PAGED_EINVAL;
+  }
+  for (i = 0; i < n; ++i) {
+    v.kind[pages[i]] = KIND_FREE;
+    v.stack[v.h->n_free++] = pages[i];
+  }
+  return PAGED_OK;
+}
+
+int paged_pool_claim_run(void* state, int32_t k, int32_t* first) {
+  View v;
+  if (!view_of(state, &v) || k < 1 || k > v.h->n_pages || first == nullptr) return PAGED_EINVAL;
+  // the highest k consecutive free pages
+  int32_t found = -1, len = 0;
+  for (int32_t p = v.h->n_pages - 1; p >= 0; --p) {
+    len = v.kind[p] == KIND_FREE ? len + 1 : 0;
+    if (len == k) {
+      found = p;
+      break;
+    }
+  }
+  if (found < 0) return PAGED_EFULL;  // too fragmented for the run: the request waits
+  for (int32_t p = found; p < found + k; ++p) v.kind[p] = KIND_RUN;
+  // drop the run's pages from the free stack, keeping the order of the rest
+  int32_t w = 0;
+  for (int32_t i = 0; i < v.h->n_free; ++i) {
+    const int32_t p = v.stack[i];
+    if (v.kind[p] == KIND_FREE) v.stack[w++] = p;
+  }
+  v.h->n_free = w;
+  *first = found;
+  return PAGED_OK;
+}
+
+int paged_pool_release_run(void* state, int32_t first, int32_t k) {
+  View v;
+  if (!view_of(state, &v) || k < 1 || first < 0 || (int64_t)first + k > v.h->n_pages) return PAGED_EINVAL;
+  for (int32_t p = first; p < first + k; ++p)
+    if (v.kind[p] != KIND_RUN) return PAGED_EINVAL;
+  // pushed from the top page down, so the run's lowest page comes off the stack first
+  for (int32_t p = first + k - 1; p >= first; --p) {
+    v.kind[p] = KIND_FREE;
+    v.stack[v.h->n_free++] = p;
+  }
+  return PAGED_OK;
+}
+
+}  // extern "C"

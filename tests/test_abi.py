@@ -18,7 +18,7 @@ MIS = FAKE + 4          # misaligned
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(paged_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int32_t|int|size_t|const char \*)\s*(paged_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():

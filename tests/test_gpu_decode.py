@@ -201,3 +201,43 @@ def test_workspace_reuse_with_changing_inputs():
         qf = (qb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         ref = O.decode(qf, K, V, lens, 1 / 16)
         assert rel_err_rows(out.cpu().numpy(), ref) <= TOL, (it, lens)
+
+
+def test_tables_from_the_page_pool_after_churn():
+    """Page tables built by the library's host pool while streams grow page by page, a transient
+    stream takes and returns pages and runs are claimed from the top (fragmented tables): paged ==
+    contiguous bit for bit and within the bound of the oracle."""
+    ptok, lens = 48, [3000, 1500, 700]
+    need = [(L + ptok - 1) // ptok for L in lens]
+    n_pages = sum(need) + 40
+    st = np.zeros(P.paged_pool_state_bytes(n_pages), np.uint8)
+    P.paged_pool_init(st, n_pages)
+    rng = np.random.default_rng(11)
+    table = np.zeros((3, max(need)), np.int32)
+    have = [0, 0, 0]
+    one = np.zeros(8, np.int32)
+    transient, runs = [], []
+    while have != need:
+        s = int(rng.integers(0, 3))
+        if have[s] < need[s]:
+            assert P.paged_pool_alloc(st, 1, one) == P.PAGED_OK
+            table[s, have[s]] = one[0]
+            have[s] += 1
+        r = rng.random()
+        if r < 0.3 and P.paged_pool_alloc(st, 2, one) == P.PAGED_OK:
+            transient.extend(one[:2].tolist())
+        elif r < 0.5 and transient:
+            k = int(rng.integers(1, len(transient) + 1))
+            give = transient[:k]
+            transient = transient[k:]
+            P.paged_pool_free(st, np.array(give[::-1], np.int32), len(give))
+        elif r < 0.55:
+            first = P.paged_pool_claim_run(st, 3)
+            if first != P.PAGED_EFULL:
+                runs.append(first)
+    assert len(set(table[s, i] for s in range(3) for i in range(need[s]))) == sum(need)
+    w = make_workload(12, lens, ptok, 16, 4, dtype="bf16", table_kind="shuffled")
+    w.table, w.n_pages = table, n_pages
+    pl, pc, q, out = _run_case(w, 1 / 16)
+    err = rel_err_rows(out, _oracle(w, 1 / 16))
+    assert err <= TOL, err

@@ -1,0 +1,147 @@
+"""Host page pool (CPU only): the model written from the pages is pinned by hand-worked
+sequences, and the library's pool (through the C ABI) must agree with the model, page id for
+page id, over random sequences of requests.
+
+TensorFold PR #1170, commit 1ac2075: the free stack hands out KV pages from the bottom;
+runs of k consecutive free pages come from the top; a pool too fragmented for a run makes the
+request wait.
+"""
+import numpy as np
+import pytest
+
+import paged_kv_cache_pg_amd as P
+from oracle.pool_model import PagePool
+
+
+# ---- pins of the model (hand-worked from the pages' rules) ----
+
+def test_model_fresh_pool_hands_out_from_the_bottom():
+    m = PagePool(10)
+    assert m.alloc(3) == [0, 1, 2]
+    assert m.alloc(2) == [3, 4]
+    assert m.free_count() == 5
+
+
+def test_model_runs_come_from_the_top():
+    m = PagePool(10)
+    assert m.alloc(2) == [0, 1]
+    assert m.claim_run(3) == 7          # pages 7, 8, 9
+    assert m.claim_run(2) == 5          # pages 5, 6
+    assert m.alloc(3) == [2, 3, 4]      # the stack still hands out from the bottom
+    assert m.claim_run(1) is None       # nothing free: the request waits
+    assert m.free_count() == 0
+
+
+def test_model_freed_pages_are_reused_last_in_first_out():
+    m = PagePool(6)
+    assert m.alloc(4) == [0, 1, 2, 3]
+    assert m.free([2, 0])
+    assert m.alloc(2) == [0, 2]         # the last page freed comes back first
+    assert m.alloc(1) == [4]
+
+
+def test_model_fragmented_pool_refuses_a_run():
+    m = PagePool(8)
+    got = m.alloc(8)
+    assert got == list(range(8))
+    assert m.free([1, 3, 5, 7])         # four free pages, no two adjacent
+    assert m.claim_run(2) is None       # too fragmented: the request waits
+    assert m.claim_run(1) == 7          # the highest single free page
+    assert m.free([6])                  # free now: 1, 3, 5, 6
+    assert m.claim_run(2) == 5          # pages 5 and 6
+    assert m.claim_run(2) is None       # free now: 1, 3
+    assert m.release_run(7, 1)          # free now: 1, 3, 7
+    assert m.alloc(3) == [7, 3, 1]      # last in, first out
+
+
+def test_model_release_puts_the_run_lowest_page_on_top():
+    m = PagePool(5)
+    assert m.claim_run(3) == 2
+    assert m.alloc(2) == [0, 1]
+    assert m.release_run(2, 3)
+    assert m.alloc(3) == [2, 3, 4]
+
+
+def test_model_refusals_change_nothing():
+    m = PagePool(4)
+    assert m.alloc(5) is None and m.free_count() == 4
+    assert m.alloc(2) == [0, 1]
+    assert not m.free([1, 1])           # listed twice
+    assert not m.free([2])              # never handed out
+    assert not m.release_run(0, 2)      # pages, not a run
+    assert m.free_count() == 2 and m.alloc(2) == [2, 3]
+
+
+# ---- the library against the model ----
+
+def _lib_pool(n):
+    st = np.zeros(P.paged_pool_state_bytes(n), np.uint8)
+    P.paged_pool_init(st, n)
+    return st
+
+
+def test_library_pool_hand_worked_sequence():
+    st = _lib_pool(10)
+    pages = np.zeros(16, np.int32)
+    assert P.paged_pool_alloc(st, 2, pages) == P.PAGED_OK and list(pages[:2]) == [0, 1]
+    assert P.paged_pool_claim_run(st, 3) == 7
+    assert P.paged_pool_claim_run(st, 2) == 5
+    assert P.paged_pool_alloc(st, 3, pages) == P.PAGED_OK and list(pages[:3]) == [2, 3, 4]
+    assert P.paged_pool_claim_run(st, 1) == P.PAGED_EFULL
+    assert P.paged_pool_alloc(st, 1, pages) == P.PAGED_EFULL
+    assert P.paged_pool_free_count(st) == 0
+
+
+def test_library_pool_refusals():
+    st = _lib_pool(4)
+    pages = np.zeros(8, np.int32)
+    assert P.paged_pool_alloc(st, 2, pages) == P.PAGED_OK
+    with pytest.raises(P.PagedError):
+        P.paged_pool_free(st, np.array([1, 1], np.int32), 2)
+    with pytest.raises(P.PagedError):
+        P.paged_pool_free(st, np.array([3], np.int32), 1)
+    with pytest.raises(P.PagedError):
+        P.paged_pool_release_run(st, 0, 2)
+    assert P.paged_pool_free_count(st) == 2
+    bad = np.zeros(64, np.uint8)        # never initialised
+    with pytest.raises(P.PagedError):
+        P.paged_pool_free_count(bad)
+    assert P.paged_pool_state_bytes(0) == 0
+
+
+@pytest.mark.parametrize("seed,n", [(1, 16), (2, 64), (3, 257), (4, 1000)])
+def test_library_pool_matches_model_on_random_requests(seed, n):
+    rng = np.random.default_rng(seed)
+    st, m = _lib_pool(n), PagePool(n)
+    held_pages, held_runs = [], []
+    buf = np.zeros(n, np.int32)
+    for _ in range(600):
+        op = rng.integers(0, 4)
+        if op == 0:
+            k = int(rng.integers(0, max(2, n // 8)))
+            want = m.alloc(k)
+            got = P.paged_pool_alloc(st, k, buf)
+            if want is None:
+                assert got == P.PAGED_EFULL
+            else:
+                assert got == P.PAGED_OK and list(buf[:k]) == want
+                held_pages.extend(want)
+        elif op == 1 and held_pages:
+            k = int(rng.integers(1, len(held_pages) + 1))
+            idx = rng.choice(len(held_pages), size=k, replace=False)
+            give = [held_pages[i] for i in idx]
+            held_pages = [p for i, p in enumerate(held_pages) if i not in set(idx.tolist())]
+            assert m.free(give)
+            P.paged_pool_free(st, np.array(give, np.int32), len(give))
+        elif op == 2:
+            k = int(rng.integers(1, max(2, n // 6)))
+            want = m.claim_run(k)
+            got = P.paged_pool_claim_run(st, k)
+            assert got == (P.PAGED_EFULL if want is None else want)
+            if want is not None:
+                held_runs.append((want, k))
+        elif op == 3 and held_runs:
+            first, k = held_runs.pop(int(rng.integers(0, len(held_runs))))
+            assert m.release_run(first, k)
+            P.paged_pool_release_run(st, first, k)
+        assert P.paged_pool_free_count(st) == m.free_count()
