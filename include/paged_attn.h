@@ -225,6 +225,30 @@ int paged_rows_gather(void *dst, int64_t stride_s, int64_t stride_h, int64_t str
                       int32_t n_streams, int32_t max_len, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Append a step's rows ([P1 "What this changes": fn_attn_prep stores keys, values and
+ * indexer keys through pg_at; the pool kernel reads and writes through pg_at once per
+ * block of four]).
+ *
+ * For each stream s the n_new new tokens sit at positions pos0[s] .. pos0[s]+n_new-1
+ * (positions at or past max_len are dropped; pos0 is clamped to [0, max_len]).  Their K
+ * and V rows (all heads) and indexer-key rows are stored through the table, and every
+ * block of four whose last position is among the new ones gets its pooled row
+ * float32(((IK[4b] + IK[4b+1]) + IK[4b+2]) + IK[4b+3]) / 4) (float64 sum), the value
+ * paged_pool_blocks writes: rows before pos0[s] are read from the arena (stored by
+ * earlier steps), the new ones from ik_new.  One launch.
+ *   k_new, v_new device [n_streams][n_new][n_kv_heads][head_dim], kv->dtype, 16-byte aligned
+ *   ik_new       device [n_streams][n_new][idx_dim] of kv->dtype, or NULL (no indexer keys:
+ *                ik, pooled and idx_dim are ignored)
+ *   kv           K and V region bases; ik, pooled: region bases as for paged_pool_blocks
+ *   pos0         device [n_streams] int32
+ * page_pos must be a multiple of 4 when ik_new is given.  The caller must not run two
+ * appends that write the same rows concurrently.
+ */
+int paged_kv_append(const void *k_new, const void *v_new, const void *ik_new, int32_t n_new,
+                    const paged_kv *kv, void *ik, void *pooled, int32_t idx_dim, const paged_pg *pg,
+                    const int32_t *pos0, int32_t n_streams, int32_t max_len, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Test hook: the row addressing itself, on the device.  out[i] = the element
  * offset of row (streams[i], heads[i], positions[i]) in a region whose page
  * part is [H][page_pos][row_width] -- the same device function every kernel

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     paged_attn_prefill,
     paged_attn_prefill_workspace,
     paged_block_scores_topk,
+    paged_kv_append,
     paged_pool_alloc,
     paged_pool_blocks,
     paged_pool_claim_run,

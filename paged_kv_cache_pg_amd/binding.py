@@ -71,6 +71,8 @@ _SIGS = {
     "paged_row_offsets": (c_int32, [POINTER(PgStruct), c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_void_p]),
     "paged_strerror": (ctypes.c_char_p, [c_int32]),
+    "paged_kv_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, POINTER(KvStruct), c_void_p, c_void_p,
+                                  c_int32, POINTER(PgStruct), c_void_p, c_int32, c_int32, c_void_p]),
     "paged_pool_state_bytes": (c_size_t, [c_int32]),
     "paged_pool_init": (c_int32, [c_void_p, c_size_t, c_int32]),
     "paged_pool_alloc": (c_int32, [c_void_p, c_int32, c_void_p]),
@@ -215,6 +217,13 @@ def paged_row_offsets(pg: PgStruct, n_streams: int, row_width: int, streams, hea
                       stream=None):
     _check(lib().paged_row_offsets(ctypes.byref(pg), n_streams, row_width, _p(streams), _p(heads), _p(positions),
                                    _p(out), n, _stream(stream)), "paged_row_offsets")
+
+
+def paged_kv_append(k_new, v_new, ik_new, n_new: int, kv: KvStruct, ik, pooled, idx_dim: int, pg: PgStruct, pos0,
+                    n_streams: int, max_len: int, stream=None):
+    _check(lib().paged_kv_append(_p(k_new), _p(v_new), _p(ik_new), n_new, ctypes.byref(kv), _p(ik), _p(pooled),
+                                 idx_dim, ctypes.byref(pg), _p(pos0), n_streams, max_len, _stream(stream)),
+           "paged_kv_append")
 
 
 # ---------------------------------------------------------------------------

@@ -292,6 +292,46 @@ int paged_rows_gather(void* dst, int64_t stride_s, int64_t stride_h, int64_t str
                      pos_end, n_streams, max_len, stream);
 }
 
+int paged_kv_append(const void* k_new, const void* v_new, const void* ik_new, int32_t n_new, const paged_kv* kv,
+                    void* ik, void* pooled, int32_t idx_dim, const paged_pg* pg, const int32_t* pos0,
+                    int32_t n_streams, int32_t max_len, hipStream_t stream) {
+  if (n_new < 0 || n_streams < 0 || max_len < 0 || max_len > MAX_POS) return PAGED_EINVAL;
+  int r = check_kv(kv, pg);
+  if (r) return r;
+  const bool has_ik = ik_new != nullptr;
+  r = check_pg(pg, kv->dtype, max_len, has_ik);
+  if (r) return r;
+  const int es = esize(kv->dtype);
+  const int64_t kv_bytes = (int64_t)kv->n_kv_heads * pg->page_pos * kv->head_dim * es;
+  if (has_ik) {
+    if (idx_dim < 8 || idx_dim > 1024 || idx_dim % 8 != 0) return PAGED_EINVAL;
+    if (ik == nullptr || pooled == nullptr || !al(ik, 16) || !al(pooled, 16) || !al(ik_new, 16)) return PAGED_EINVAL;
+    if (pg->page_elems * es < 2 * kv_bytes + (int64_t)pg->page_pos * idx_dim * es + (int64_t)(pg->page_pos / 4) * idx_dim * 4)
+      return PAGED_EINVAL;
+  }
+  if (n_streams == 0 || n_new == 0) return PAGED_OK;
+  if (k_new == nullptr || v_new == nullptr || !al(k_new, 16) || !al(v_new, 16)) return PAGED_EINVAL;
+  if (pos0 == nullptr || !al(pos0, 4)) return PAGED_EINVAL;
+  AppendArgs a;
+  a.k_new = (const char*)k_new;
+  a.v_new = (const char*)v_new;
+  a.ik_new = (const char*)ik_new;
+  a.kb = (char*)kv->k;
+  a.vb = (char*)kv->v;
+  a.ikb = (char*)ik;
+  a.pooled = (char*)pooled;
+  a.pg = to_dev(pg, kv->dtype);
+  a.pos0 = pos0;
+  a.n = n_new;
+  a.hkv = kv->n_kv_heads;
+  a.row_bytes = kv->head_dim * es;
+  a.ik_row_bytes = has_ik ? idx_dim * es : 0;
+  a.idx_dim = has_ik ? idx_dim : 8;
+  a.max_len = max_len;
+  a.bf16 = kv->dtype == PAGED_BF16;
+  return hip_status(launch_append(a, n_streams, stream));
+}
+
 int paged_row_offsets(const paged_pg* pg, int32_t n_streams, int32_t row_width, const int32_t* streams,
                       const int32_t* heads, const int32_t* positions, int64_t* out, int32_t n, hipStream_t stream) {
   if (pg == nullptr || pg->reserved != 0 || pg->page_pos < 1 || pg->page_elems < 1) return PAGED_EINVAL;

@@ -94,6 +94,26 @@ struct RowsArgs {
 };
 hipError_t launch_rows(const RowsArgs& a, hipStream_t st);
 
+struct AppendArgs {
+  const char* k_new;      // [S][n][Hkv][row] token-major step rows
+  const char* v_new;
+  const char* ik_new;     // [S][n][DI] or nullptr (no indexer keys)
+  char* kb;               // region bases (page 0)
+  char* vb;
+  char* ikb;
+  char* pooled;
+  PgDev pg;               // page_bytes of the arena
+  const int32_t* pos0;    // [S] position of each stream's first new token
+  int32_t n;              // new tokens a stream
+  int32_t hkv;
+  int32_t row_bytes;      // K / V row
+  int32_t ik_row_bytes;   // indexer-key row (0: none)
+  int32_t idx_dim;
+  int32_t max_len;
+  int32_t bf16;           // arena element type
+};
+hipError_t launch_append(const AppendArgs& a, int n_streams, hipStream_t st);
+
 struct OffArgs {
   PgDev pg;               // page_bytes holds page_elems (element units) for this hook
   int32_t n_streams;

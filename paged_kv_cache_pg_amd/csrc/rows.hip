@@ -42,7 +42,92 @@ __global__ __launch_bounds__(256) void row_offsets_kernel(OffArgs a) {
   a.out[i] = r;
 }
 
+// One step's rows in, through the table, and the pooled row of every block of four the step
+// completes.  Per stream: item = (token, 16-byte chunk of its K, V or indexer-key row), then
+// item = (completed block, 8 dims).  A completed block's rows at positions before the step come
+// from the arena (stored by earlier steps), the others from the step's input, so no item waits
+// for another; the pooled value is the same float64 sum, in row order, that pool_kernel forms.
+template <bool BF16>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int s = blockIdx.y;
+  const int p0 = min(max(a.pos0[s], 0), a.max_len);
+  const int nn = max(0, min(a.n, a.max_len - p0));
+  if (nn == 0) return;
+  const int cpr = a.row_bytes / 16, icpr = a.ik_row_bytes / 16;
+  const int per_tok = 2 * a.hkv * cpr + icpr;
+  const int64_t items_a = (int64_t)nn * per_tok;
+  const int b_lo = p0 / 4, b_hi = a.ik_row_bytes ? (p0 + nn) / 4 : b_lo;  // blocks whose last row is new
+  const int cpb = a.idx_dim / 8;
+  const int64_t items = items_a + (int64_t)(b_hi - b_lo) * cpb;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    if (it < items_a) {
+      const int t = (int)(it / per_tok);
+      const int r = (int)(it - (int64_t)t * per_tok);
+      const int p = p0 + t;
+      const int64_t tok = (int64_t)s * a.n + t;
+      if (r < 2 * a.hkv * cpr) {
+        const int v = r >= a.hkv * cpr;
+        const int rr = r - v * a.hkv * cpr;
+        const int h = rr / cpr, c = rr - h * cpr;
+        const char* src = (v ? a.v_new : a.k_new) + (tok * a.hkv + h) * a.row_bytes + 16 * c;
+        char* dst = (v ? a.vb : a.kb) + pg_at(a.pg, s, h, p, a.row_bytes) + 16 * c;
+        *(uint4*)dst = *(const uint4*)src;
+      } else {
+        const int c = r - 2 * a.hkv * cpr;
+        const char* src = a.ik_new + tok * a.ik_row_bytes + 16 * c;
+        char* dst = a.ikb + pg_at(a.pg, s, 0, p, a.ik_row_bytes) + 16 * c;
+        *(uint4*)dst = *(const uint4*)src;
+      }
+    } else {
+      const int64_t j = it - items_a;
+      const int b = b_lo + (int)(j / cpb);
+      const int c8 = (int)(j - (int64_t)(b - b_lo) * cpb);
+      float x[4][8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 4 * b + r;
+        const char* row = p >= p0 ? a.ik_new + ((int64_t)s * a.n + (p - p0)) * a.ik_row_bytes
+                                  : a.ikb + pg_at(a.pg, s, 0, p, a.ik_row_bytes);
+        const char* src = row + c8 * 8 * ES;
+        if constexpr (BF16) {
+          const uint4 u = *(const uint4*)src;
+          x[r][0] = bf16lo(u.x); x[r][1] = bf16hi(u.x); x[r][2] = bf16lo(u.y); x[r][3] = bf16hi(u.y);
+          x[r][4] = bf16lo(u.z); x[r][5] = bf16hi(u.z); x[r][6] = bf16lo(u.w); x[r][7] = bf16hi(u.w);
+        } else {
+          const float4 u = *(const float4*)src, w = *(const float4*)(src + 16);
+          x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
+          x[r][4] = w.x; x[r][5] = w.y; x[r][6] = w.z; x[r][7] = w.w;
+        }
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double acc = (double)x[0][e] + (double)x[1][e];
+        acc = acc + (double)x[2][e];
+        acc = acc + (double)x[3][e];
+        y[e] = (float)(acc * 0.25);
+      }
+      float4* dst = (float4*)(a.pooled + pool_at(a.pg, s, b, a.idx_dim * 4) + c8 * 32);
+      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int n_streams, hipStream_t st) {
+  if (n_streams <= 0 || a.n <= 0 || a.max_len <= 0) return hipSuccess;
+  const int cpr = a.row_bytes / 16, icpr = a.ik_row_bytes / 16;
+  const int64_t items = (int64_t)a.n * (2 * a.hkv * cpr + icpr) + (int64_t)((a.n + 3) / 4 + 1) * (a.idx_dim / 8);
+  int gx = (int)((items + 255) / 256);
+  if (gx > 4096) gx = 4096;
+  if (gx < 1) gx = 1;
+  if (a.bf16) hipLaunchKernelGGL(append_kernel<true>, dim3(gx, n_streams), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(append_kernel<false>, dim3(gx, n_streams), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_rows(const RowsArgs& a, hipStream_t st) {
   if (a.n_streams <= 0 || a.max_len <= 0) return hipSuccess;
