@@ -9,9 +9,9 @@ K/V and q, fp32 accumulation, one query token a stream.  ``value`` is the
 decode's algorithmic HBM bytes (K/V rows, q, table, lengths, output) over its
 measured time, in GB/s.  The line also carries the roofline of the decode,
 the float64 oracle timed on the host cores, and the other rows of the path
-(chunked prefill, block pooling, scores + top-k, sparse attention) as extra
-objects.  Inputs are seeded synthetic N(0, 1) draws; they sit in HBM before
-timing starts.  Two copies of the arena alternate between steps so the
+(chunked prefill, block pooling, scores + top-k, sparse attention, the
+appends of a decode step and a prefill chunk) as extra objects.  Inputs are
+seeded synthetic N(0, 1) draws; they sit in HBM before timing starts.  Two copies of the arena alternate between steps so the
 256 MB Infinity Cache cannot serve a step from the previous one.
 """
 from __future__ import annotations
@@ -301,6 +301,79 @@ class SparseBench:
         return ok, err
 
 
+class AppendBench:
+    """paged_kv_append into pages of 256 (shuffled), 4 KV heads, head dim 256, 128-wide indexer keys, bf16:
+    a decode step (4 streams x 1 token at position 4095, which completes a block of four) and a prefill chunk
+    (1 stream x 2048 tokens at position 2048)."""
+    HKV, D, DI, PTOK = 4, 256, 128, 256
+
+    def __init__(self, n_streams: int, n_new: int, pos0: int, seed: int = 6):
+        import numpy as np
+        import torch
+        import paged_kv_cache_pg_amd as P
+        from paged_kv_cache_pg_amd.inputs import make_table
+        self.P, self.torch = P, torch
+        S, L = n_streams, pos0 + n_new
+        lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_BF16, idx_dim=self.DI)
+        rng = np.random.default_rng(seed)
+        table, n_pages = make_table("shuffled", [(L + self.PTOK - 1) // self.PTOK] * S, rng)
+        self.table = torch.from_numpy(table.astype(np.int32)).cuda()
+        self.pg = P.make_pg(self.table, self.PTOK, lay.page_elems)
+        self.arena = torch.zeros(n_pages * lay.page_bytes, dtype=torch.uint8, device="cuda")
+        base = self.arena.data_ptr()
+        self.kv = P.make_kv(base + lay.k_off, base + lay.v_off, P.PAGED_BF16, self.HKV, self.D)
+        self.ik, self.pooled = base + lay.ik_off, base + lay.pool_off
+        self.k_new = torch.randn((S, n_new, self.HKV, self.D), device="cuda").to(torch.bfloat16)
+        self.v_new = torch.randn((S, n_new, self.HKV, self.D), device="cuda").to(torch.bfloat16)
+        self.ik_new = torch.randn((S, n_new, self.DI), device="cuda").to(torch.bfloat16)
+        self.pos0 = torch.full((S,), pos0, dtype=torch.int32, device="cuda")
+        self.S, self.n, self.L = S, n_new, L
+        n_blocks = S * ((pos0 + n_new) // 4 - pos0 // 4)
+        # K, V and indexer-key rows read and written once, pooled rows written once
+        self.bytes = 2 * S * n_new * (2 * self.HKV * self.D * 2 + self.DI * 2) + n_blocks * self.DI * 4
+
+    def step(self, i=0):
+        self.P.paged_kv_append(self.k_new, self.v_new, self.ik_new, self.n, self.kv, self.ik, self.pooled, self.DI,
+                               self.pg, self.pos0, self.S, self.L)
+
+
+def time_graph(fn, steps: int, warmup: int):
+    """K calls captured in one HIP graph and replayed, timed with HIP events around a replay: the GPU
+    time of calls too short for the host to issue back to back (the calls allocate nothing and record
+    no memset)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(1, warmup)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def run_append(args):
+    out = {}
+    for name, (S, n, p0) in (("decode_step_4x1", (4, 1, 4095)), ("prefill_chunk_1x2048", (1, 2048, 2048))):
+        ab = AppendBench(S, n, p0)
+        ms = time_graph(ab.step, args.steps, args.warmup)
+        out[name] = {"us": round(ms * 1e3, 2), "bytes": ab.bytes, "GB_per_s": round(ab.bytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"append {name}: {ms * 1e3:.1f} us, {ab.bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+        del ab
+    return out
+
+
 def time_steps(fn, steps: int, warmup: int):
     """Warm-up, then K steps bracketed by a synchronize and a pair of HIP events on the current stream
     (the stream the library launches on).  Returns (ms per step, wall seconds)."""
@@ -406,7 +479,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "sparse"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "sparse", "append"], default=None,
                     help="run one row only (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -441,6 +514,9 @@ def main():
         torch.cuda.empty_cache()
     if args.only in (None, "sparse"):
         result["sparse"] = run_sparse(args)
+        torch.cuda.empty_cache()
+    if args.only in (None, "append"):
+        result["append"] = run_append(args)
         torch.cuda.empty_cache()
     if args.only is None and not args.no_cpu_baseline:
         result["cpu_baseline"] = DecodeBench.cpu_baseline_from_scratch()

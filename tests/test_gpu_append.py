@@ -83,8 +83,8 @@ def test_append_steps_equal_oracle_arena(ptok):
 
 
 def test_append_contiguous_and_one_token_steps():
-    """No table (contiguous form), one token a step for 61 steps (a decode loop)."""
-    L = 61
+    """No table (contiguous form; rows a head a multiple of 4), one token a step for 64 steps (a decode loop)."""
+    L = 64
     w = make_workload(72, [L, L, L], 16, 16, HKV, dtype="bf16", table_kind=None, idx_dim=DI, n_idx_heads=4)
     got = _append_all(w, None, 3, L, [1] * L)
     want = _expected_arena(w, None, 3, L)
