@@ -16,4 +16,11 @@ from .paged_oracle import (  # noqa: F401
     pool,
     scores,
     topk,
+    E4M3_MAX,
+    e4m3_value,
+    e4m3_encode,
+    e4m3_quantize_rows,
+    e4m3_dequantize,
+    place_fp8,
+    gather_fp8,
 )

@@ -25,6 +25,12 @@ Parity status per function:
   scores                                    : pinned (exact integer scores,
       one-hot rows, linearity)
   topk                                      : pinned (brute-force sort, ties)
+  e4m3_value / e4m3_encode                  : pinned (hand-derived codes, torch's
+      float8_e4m3fn conversion, exhaustive round trip, ties, saturation)
+  e4m3_quantize_rows / dequantize           : pinned (amax code is +-448, error
+      bound of half a code step, zero rows, scale exactness)
+  place_fp8 / gather_fp8                    : pinned (hand-derived scale offsets,
+      round trip)
 """
 from __future__ import annotations
 
@@ -33,7 +39,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-ESIZE = {"bf16": 2, "f32": 4}
+ESIZE = {"bf16": 2, "f32": 4, "fp8": 1}
 
 
 # ---------------------------------------------------------------------------
@@ -50,6 +56,12 @@ class PageLayout:
     [key, value][head][position][row].  Reading taken: K [Hkv][n][D], then
     V [Hkv][n][D], then IK [n][DI], then POOL [n/4][DI] float32.
     All offsets are in bytes.
+
+    dtype "fp8" ([P2 commit 5c09685]: a row is e4m3 codes plus an fp32 scale,
+    the page size counted in bytes): K codes [Hkv][n][D] bytes, V codes, then
+    the K scales [Hkv][n] float32 and the V scales, the page padded to 16 bytes;
+    no indexer keys.  Reading taken: the scales sit after the codes in the same
+    page, one float32 a row, in the rows' [head][position] order.
     """
     n_kv_heads: int
     head_dim: int
@@ -74,11 +86,24 @@ class PageLayout:
         return 2 * self.v_off
 
     @property
+    def ks_off(self) -> int:
+        assert self.dtype == "fp8"
+        return 2 * self.v_off
+
+    @property
+    def vs_off(self) -> int:
+        return self.ks_off + self.n_kv_heads * self.page_pos * 4
+
+    @property
     def pool_off(self) -> int:
         return self.ik_off + self.page_pos * self.idx_dim * self.esize
 
     @property
     def page_bytes(self) -> int:
+        if self.dtype == "fp8":
+            assert self.idx_dim == 0
+            end = self.vs_off + self.n_kv_heads * self.page_pos * 4
+            return (end + 15) // 16 * 16
         if self.idx_dim == 0:
             return self.ik_off
         return self.pool_off + (self.page_pos // 4) * self.idx_dim * 4
@@ -338,3 +363,127 @@ def topk(score: np.ndarray, k: int) -> np.ndarray:
     ids = np.arange(nb)
     order = np.lexsort((ids, -score))
     return np.sort(order[:min(k, nb)])
+
+
+# ---------------------------------------------------------------------------
+# e4m3 rows with one float32 scale a row
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of each e4m3 code as float64, from the format's definition.
+
+    OCP 8-bit floating point, E4M3 ("fn": finite only): bit 7 is the sign,
+    bits 6..3 the exponent with bias 7, bits 2..0 the mantissa.  An exponent
+    field of 0 is subnormal, m/8 * 2^-6; otherwise (1 + m/8) * 2^(e-7).
+    S.1111.111 is NaN; there are no infinities, so S.1111.110 = 448 is the
+    largest magnitude.  [P2 commit 5c09685]: rows are e4m3 codes and the
+    reference dequantizes e4m3 x scale in float64.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """e4m3 code of each float32 value: the nearest finite e4m3 value, ties to
+    the even code; magnitudes beyond 448 become 448; the sign bit is kept (so
+    -0.0 -> 0x80).  NaN is not accepted.
+
+    Readings: round to nearest even, as for every IEEE-style narrowing; the
+    pages' store saturates rather than producing NaN (the format has no
+    infinity).  Done by brute force over the table of the 127 non-negative
+    finite values (codes 0..126, which increase with the code).
+    """
+    y = np.asarray(y, dtype=np.float32)
+    assert not np.isnan(y).any()
+    table = e4m3_value(np.arange(127))
+    mag = np.minimum(np.abs(y.astype(np.float64)), E4M3_MAX).reshape(-1)
+    out = np.empty(mag.shape, dtype=np.int64)
+    step = 1 << 14
+    for i in range(0, mag.size, step):
+        d = np.abs(mag[i:i + step, None] - table[None, :])     # exact in float64
+        best = np.argmin(d, axis=1)                              # the lower code on a tie
+        nxt = np.minimum(best + 1, 126)
+        tie = (d[np.arange(best.size), nxt] == d[np.arange(best.size), best]) & (nxt != best)
+        best = np.where(tie & (best % 2 == 1), nxt, best)       # the even one of the two
+        out[i:i + step] = best
+    sign = np.signbit(y.reshape(-1)).astype(np.int64) << 7
+    return (out | sign).astype(np.uint8).reshape(y.shape)
+
+
+def e4m3_quantize_rows(x) -> tuple:
+    """Codes and scale of each row (last axis) of float32 values.
+
+    scale = amax / 448 with amax = max |x| over the row, a float32 quotient;
+    code = e4m3_encode(x / scale), float32 quotients; a row of zeros gets scale
+    0 and codes 0.  [P2 commit 5c09685] names the store (codes plus an fp32
+    scale a row) but not the scale rule: this absmax-to-448 rule is the
+    reading, so that code x scale spans the row's range.  Returns (codes
+    uint8 [..., D], scales float32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    live = amax > 0
+    div = np.where(live, scale, np.float32(1.0)).astype(np.float32)
+    codes = e4m3_encode((x / div[..., None]).astype(np.float32))
+    codes = np.where(live[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, np.where(live, scale, np.float32(0.0)).astype(np.float32)
+
+
+def e4m3_dequantize(codes, scales) -> np.ndarray:
+    """code x scale in float64 (exact: 4 significant bits times 24)."""
+    return e4m3_value(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def place_fp8(layout: PageLayout, table, n_pages: int, lens: Sequence[int], KC, VC, KS, VS) -> np.ndarray:
+    """Write e4m3 rows and their scales into a fresh zero arena (bytes) through the table.
+
+    KC, VC: [S][Hkv][cap][D] uint8 codes; KS, VS: [S][Hkv][cap] float32 scales.
+    A row's codes sit at row_offset(..., width=D) in the code regions and its
+    scale at row_offset(..., width=4) (bytes) in the scale regions: the same
+    page lookup, rows of 4 bytes.
+    """
+    assert layout.dtype == "fp8"
+    arena = np.zeros(n_pages * layout.page_bytes, dtype=np.uint8)
+    D = layout.head_dim
+    pe = layout.page_elems
+    for s, L in enumerate(lens):
+        for h in range(layout.n_kv_heads):
+            for p in range(int(L)):
+                o = row_offset(table, layout.page_pos, pe, s, h, p, D)
+                arena[layout.k_off + o:layout.k_off + o + D] = KC[s, h, p]
+                arena[layout.v_off + o:layout.v_off + o + D] = VC[s, h, p]
+                so = row_offset(table, layout.page_pos, pe, s, h, p, 4)
+                arena[layout.ks_off + so:layout.ks_off + so + 4] = np.frombuffer(np.float32(KS[s, h, p]).tobytes(), np.uint8)
+                arena[layout.vs_off + so:layout.vs_off + so + 4] = np.frombuffer(np.float32(VS[s, h, p]).tobytes(), np.uint8)
+    return arena
+
+
+def gather_fp8(layout: PageLayout, table, arena: np.ndarray, lens: Sequence[int], cap: Optional[int] = None):
+    """Inverse of place_fp8(): (KC, VC, KS, VS) read one row at a time through row_offset()."""
+    D = layout.head_dim
+    pe = layout.page_elems
+    cap = int(cap if cap is not None else max(list(lens) + [1]))
+    S, H = len(lens), layout.n_kv_heads
+    KC = np.zeros((S, H, cap, D), dtype=np.uint8)
+    VC = np.zeros_like(KC)
+    KS = np.zeros((S, H, cap), dtype=np.float32)
+    VS = np.zeros_like(KS)
+    for s, L in enumerate(lens):
+        for h in range(H):
+            for p in range(int(L)):
+                o = row_offset(table, layout.page_pos, pe, s, h, p, D)
+                KC[s, h, p] = arena[layout.k_off + o:layout.k_off + o + D]
+                VC[s, h, p] = arena[layout.v_off + o:layout.v_off + o + D]
+                so = row_offset(table, layout.page_pos, pe, s, h, p, 4)
+                KS[s, h, p] = arena[layout.ks_off + so:layout.ks_off + so + 4].view(np.float32)[0]
+                VS[s, h, p] = arena[layout.vs_off + so:layout.vs_off + so + 4].view(np.float32)[0]
+    return KC, VC, KS, VS

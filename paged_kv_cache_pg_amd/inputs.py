@@ -25,6 +25,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 __all__ = [
+    "draw_e4m3_codes",
+    "draw_row_scales",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "Workload",
@@ -54,6 +56,18 @@ def _draw(rng: np.random.Generator, shape, dtype: str):
     if dtype == "f32":
         return x
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def draw_e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform e4m3 codes (uint8) over the 254 codes that are not NaN (0x7F and 0xFF excluded),
+    so every magnitude from the subnormals to 448 and both signs appear."""
+    i = rng.integers(0, 254, size=shape, dtype=np.int64)
+    return (i + (i >= 0x7F)).astype(np.uint8)
+
+
+def draw_row_scales(rng: np.random.Generator, shape, lo: float = 2.0 ** -8, hi: float = 2.0 ** -5) -> np.ndarray:
+    """Positive float32 row scales, log-uniform in [lo, hi)."""
+    return np.exp2(rng.uniform(np.log2(lo), np.log2(hi), size=shape)).astype(np.float32)
 
 
 def make_table(kind: Optional[str], pages_per_stream: Sequence[int], rng: Optional[np.random.Generator] = None,
