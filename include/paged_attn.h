@@ -61,8 +61,11 @@
 extern "C" {
 #endif
 
-/* Element types. */
-typedef enum { PAGED_F32 = 0, PAGED_BF16 = 1 } paged_dtype;
+/* Element types.  PAGED_FP8_E4M3 rows are 256 e4m3 codes (OCP E4M3: 1 sign, 4 exponent bits with
+   bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448) that stand for
+   code x scale with one float32 scale a row ([P2 commit 5c09685]: a row's e4m3 codes and fp32
+   scale, read through the row's page).  Only the K/V regions of an attention layer take this type. */
+typedef enum { PAGED_F32 = 0, PAGED_BF16 = 1, PAGED_FP8_E4M3 = 2 } paged_dtype;
 
 /* Status codes. */
 enum {
@@ -85,7 +88,12 @@ typedef struct {
 } paged_pg;
 
 /* Key and value regions of one attention layer ([P2 commit 3f5b87d]:
-   [key, value][head][position][row] inside a page). */
+   [key, value][head][position][row] inside a page).
+   PAGED_FP8_E4M3 ([P2 commit 5c09685]; page_elems then counts bytes, the pages' page size "in bytes
+   for fp8"): k and v hold the codes, [Hkv][page_pos][256] bytes a page, and k_scale / v_scale the
+   rows' float32 scales, [Hkv][page_pos] a page, addressed like rows of 4 bytes:
+     scale of (s, h, p) at byte  table[s * table_stride + p / page_pos] * page_elems + (h * page_pos + p % page_pos) * 4
+   from k_scale (v_scale).  The scale fields are read only when dtype == PAGED_FP8_E4M3. */
 typedef struct {
   const void *k;         /* device, 16-byte aligned: the K region of page 0, [Hkv][page_pos][D] a page */
   const void *v;         /* device, 16-byte aligned: the V region of page 0, same shape              */
@@ -93,6 +101,8 @@ typedef struct {
   int32_t n_kv_heads;    /* Hkv >= 1                                                                   */
   int32_t head_dim;      /* D; this build serves D = 256                                               */
   int32_t reserved;      /* must be 0                                                                  */
+  const void *k_scale;   /* PAGED_FP8_E4M3: device, 4-byte aligned, K scale region of page 0           */
+  const void *v_scale;   /* PAGED_FP8_E4M3: device, 4-byte aligned, V scale region of page 0           */
 } paged_kv;
 
 /* ------------------------------------------------------------------------ */
@@ -102,7 +112,8 @@ typedef struct {
  *
  * For every stream s and query head h: out[s][h] = softmax(scale * K q) V over
  * the L_s cached positions 0..L_s-1 of KV head h / (Hq / Hkv).
- *   q        device [n_streams][n_q_heads][256], q_dtype == kv->dtype, 16-byte aligned
+ *   q        device [n_streams][n_q_heads][256], q_dtype == kv->dtype (PAGED_BF16 for PAGED_FP8_E4M3
+ *            rows), 16-byte aligned
  *   seq_lens device [n_streams] int32; values are clamped to [0, max_len]
  *   max_len  host bound on every length; table_stride * page_pos >= max_len
  *            (page_pos >= max_len when table == NULL)
@@ -110,7 +121,9 @@ typedef struct {
  *   workspace device, >= paged_attn_decode_workspace(n_streams, n_q_heads, max_len) bytes,
  *            16-byte aligned: split partials, contents undefined after the call.  Calls that
  *            share a workspace must not overlap in time (one stream, or ordered).
- * Serves n_q_heads / n_kv_heads in {1, 2, 4, 8}, head_dim 256, F32 or BF16.
+ * Serves n_q_heads / n_kv_heads in {1, 2, 4, 8}, head_dim 256, F32, BF16 or FP8_E4M3 rows.  With
+ * e4m3 rows a key's score is scale * k_scale * (q . codes) and its value row v_scale * codes; the
+ * scales must be finite.
  */
 int paged_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
                       const paged_kv *kv, const paged_pg *pg,

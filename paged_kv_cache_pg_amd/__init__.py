@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     PAGED_EFULL,
     PAGED_OK,
     PAGED_F32,
+    PAGED_FP8_E4M3,
     PagedError,
     make_kv,
     make_pg,

@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PAGED_F32 = 0
 PAGED_BF16 = 1
-DTYPES = {"f32": PAGED_F32, "bf16": PAGED_BF16}
-ESIZE = {PAGED_F32: 4, PAGED_BF16: 2}
+PAGED_FP8_E4M3 = 2
+DTYPES = {"f32": PAGED_F32, "bf16": PAGED_BF16, "fp8": PAGED_FP8_E4M3}
+ESIZE = {PAGED_F32: 4, PAGED_BF16: 2, PAGED_FP8_E4M3: 1}
 
 PAGED_OK = 0
 PAGED_EINVAL = -1
@@ -42,7 +43,7 @@ class PgStruct(ctypes.Structure):
 
 class KvStruct(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("dtype", c_int32), ("n_kv_heads", c_int32),
-                ("head_dim", c_int32), ("reserved", c_int32)]
+                ("head_dim", c_int32), ("reserved", c_int32), ("k_scale", c_void_p), ("v_scale", c_void_p)]
 
 
 _lib = None
@@ -129,12 +130,17 @@ def make_pg(table, page_pos: int, page_elems: int, table_stride: Optional[int] =
     """The pages' Pg argument: a table (device int32 tensor [S][stride] or None), positions and elements a page."""
     if table is not None and table_stride is None:
         table_stride = int(table.shape[-1])
-    return PgStruct(_p(table), int(table_stride or 0), int(page_pos), int(page_elems), 0)
+    pg = PgStruct(_p(table), int(table_stride or 0), int(page_pos), int(page_elems), 0)
+    pg._keep = table  # a tensor passed here stays allocated while the struct lives
+    return pg
 
 
-def make_kv(k, v, dtype: int, n_kv_heads: int, head_dim: int = 256) -> KvStruct:
-    """K and V region bases (tensors or int device addresses) of one layer."""
-    return KvStruct(_p(k), _p(v), int(dtype), int(n_kv_heads), int(head_dim), 0)
+def make_kv(k, v, dtype: int, n_kv_heads: int, head_dim: int = 256, k_scale=None, v_scale=None) -> KvStruct:
+    """K and V region bases (tensors or int device addresses) of one layer; for PAGED_FP8_E4M3 also the
+    K and V scale region bases."""
+    kv = KvStruct(_p(k), _p(v), int(dtype), int(n_kv_heads), int(head_dim), 0, _p(k_scale), _p(v_scale))
+    kv._keep = (k, v, k_scale, v_scale)  # tensors passed here stay allocated while the struct lives
+    return kv
 
 
 # ---------------------------------------------------------------------------

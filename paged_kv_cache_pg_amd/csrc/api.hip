@@ -14,8 +14,11 @@ namespace {
 constexpr int64_t MAX_POS = (int64_t)1 << 30;
 
 inline bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-inline int esize(int32_t dt) { return dt == PAGED_BF16 ? 2 : 4; }
+inline int esize(int32_t dt) { return dt == PAGED_FP8_E4M3 ? 1 : dt == PAGED_BF16 ? 2 : 4; }
+// types of q, indexer keys, pooled and copied rows
 inline bool dtype_ok(int32_t dt) { return dt == PAGED_F32 || dt == PAGED_BF16; }
+// types of K/V regions
+inline bool kv_dtype_ok(int32_t dt) { return dtype_ok(dt) || dt == PAGED_FP8_E4M3; }
 
 // Page-table checks shared by every call.  need4: page_pos must hold whole blocks of four.
 int check_pg(const paged_pg* pg, int32_t dtype, int64_t max_len, bool need4) {
@@ -35,9 +38,12 @@ int check_pg(const paged_pg* pg, int32_t dtype, int64_t max_len, bool need4) {
 
 int check_kv(const paged_kv* kv, const paged_pg* pg) {
   if (kv == nullptr) return PAGED_EINVAL;
-  if (kv->reserved != 0 || !dtype_ok(kv->dtype)) return PAGED_EINVAL;
+  if (kv->reserved != 0 || !kv_dtype_ok(kv->dtype)) return PAGED_EINVAL;
   if (kv->n_kv_heads < 1) return PAGED_EINVAL;
   if (kv->k == nullptr || kv->v == nullptr || !al(kv->k, 16) || !al(kv->v, 16)) return PAGED_EINVAL;
+  if (kv->dtype == PAGED_FP8_E4M3 &&
+      (kv->k_scale == nullptr || kv->v_scale == nullptr || !al(kv->k_scale, 4) || !al(kv->v_scale, 4)))
+    return PAGED_EINVAL;
   if (kv->head_dim != HD) return PAGED_EUNSUPPORTED;
   if (pg != nullptr && pg->page_elems < (int64_t)kv->n_kv_heads * pg->page_pos * kv->head_dim) return PAGED_EINVAL;
   return PAGED_OK;
@@ -80,7 +86,9 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
   if (r) return r;
   r = group_ok(n_q_heads, kv->n_kv_heads);
   if (r) return r;
-  if (q_dtype != kv->dtype) return dtype_ok(q_dtype) ? PAGED_EUNSUPPORTED : PAGED_EINVAL;
+  // q has the rows' type; e4m3 rows take bf16 queries
+  const int32_t q_want = kv->dtype == PAGED_FP8_E4M3 ? PAGED_BF16 : kv->dtype;
+  if (q_dtype != q_want) return dtype_ok(q_dtype) ? PAGED_EUNSUPPORTED : PAGED_EINVAL;
   if (!isfinite(scale)) return PAGED_EINVAL;
   if (n_streams == 0) return PAGED_OK;
   if (q == nullptr || !al(q, 16) || out == nullptr || !al(out, 16)) return PAGED_EINVAL;
@@ -97,6 +105,9 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
   a.q = q;
   a.kb = (const char*)kv->k;
   a.vb = (const char*)kv->v;
+  const bool fp8 = kv->dtype == PAGED_FP8_E4M3;
+  a.ksb = fp8 ? (const char*)kv->k_scale : nullptr;
+  a.vsb = fp8 ? (const char*)kv->v_scale : nullptr;
   a.pg = to_dev(pg, kv->dtype);
   a.lens = lens;
   a.ids = ids;
@@ -111,7 +122,8 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
   a.part_o = (float*)ws;
   a.part_ml = (float*)((char*)a.part_o + rows * HD * sizeof(float));
   a.out = out;
-  return hip_status(launch_decode(a, kv->dtype == PAGED_BF16, n_q_heads / kv->n_kv_heads, n_streams, stream));
+  const int elem = fp8 ? 2 : kv->dtype == PAGED_BF16 ? 1 : 0;
+  return hip_status(launch_decode(a, elem, n_q_heads / kv->n_kv_heads, n_streams, stream));
 }
 
 int rows_common(int gather, void* lin, int64_t ss, int64_t sh, int64_t sp, void* region, int32_t n_heads,
@@ -299,6 +311,8 @@ int paged_kv_append(const void* k_new, const void* v_new, const void* ik_new, in
   int r = check_kv(kv, pg);
   if (r) return r;
   const bool has_ik = ik_new != nullptr;
+  const bool fp8 = kv->dtype == PAGED_FP8_E4M3;
+  if (fp8 && has_ik) return PAGED_EUNSUPPORTED;  // indexer keys are not kept in e4m3 arenas
   r = check_pg(pg, kv->dtype, max_len, has_ik);
   if (r) return r;
   const int es = esize(kv->dtype);
@@ -320,6 +334,8 @@ int paged_kv_append(const void* k_new, const void* v_new, const void* ik_new, in
   a.vb = (char*)kv->v;
   a.ikb = (char*)ik;
   a.pooled = (char*)pooled;
+  a.ksb = fp8 ? (char*)kv->k_scale : nullptr;
+  a.vsb = fp8 ? (char*)kv->v_scale : nullptr;
   a.pg = to_dev(pg, kv->dtype);
   a.pos0 = pos0;
   a.n = n_new;
@@ -329,6 +345,7 @@ int paged_kv_append(const void* k_new, const void* v_new, const void* ik_new, in
   a.idx_dim = has_ik ? idx_dim : 8;
   a.max_len = max_len;
   a.bf16 = kv->dtype == PAGED_BF16;
+  a.fp8 = fp8;
   return hip_status(launch_append(a, n_streams, stream));
 }
 

@@ -22,6 +22,14 @@
 // memory pipe never drains between phases or tiles.
 // Waves merge in order inside the workgroup, splits merge in order in the
 // combine kernel.  No atomics anywhere.
+//
+// Element types: float32 and bf16 rows (q of the same type), and e4m3 rows with
+// one float32 scale a row (TensorFold PR #1170, commit 5c09685 "--kv-cache fp8
+// through the page table too": a row's e4m3 codes and fp32 scale, the row's page
+// from the table).  For e4m3 the q rows are bf16; codes widen to bf16 exactly, so
+// a score is zscale * k_scale * (q . codes) and a probability enters PV as
+// p * v_scale (the softmax sum keeps p).  The scales of a tile's keys are read
+// through the same page lookup as its rows and staged in LDS beside key_at.
 #include "internal.h"
 
 namespace paged {
@@ -34,6 +42,12 @@ namespace {
 #endif
 #ifndef PAGED_DEC_RING_SHORT
 #define PAGED_DEC_RING_SHORT 4   // the same for streams of at most two tiles a wave
+#endif
+#ifndef PAGED_DEC_RING_FP8
+#define PAGED_DEC_RING_FP8 4     // the same for e4m3 rows
+#endif
+#ifndef PAGED_DEC_RING_FP8_SHORT
+#define PAGED_DEC_RING_FP8_SHORT 4
 #endif
 #ifndef PAGED_DEC_MAX_SPLITS
 #define PAGED_DEC_MAX_SPLITS 16  // splits a stream at most
@@ -70,6 +84,15 @@ __host__ __device__ inline int dec_splits(int n) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Row types: float32, bf16, e4m3 codes (+ float32 scale a row).
+enum : int { ET_F32 = 0, ET_BF16 = 1, ET_FP8 = 2 };
+template <int ET> struct Rows {
+  static constexpr int ROWB = ET == ET_F32 ? HD * 4 : ET == ET_BF16 ? HD * 2 : HD;  // K/V row bytes
+  static constexpr int QROWB = ET == ET_F32 ? HD * 4 : HD * 2;                    // q row bytes
+  static constexpr int NCQ = ROWB / 256;  // 16-byte K chunks a lane in QK (16 lanes a key)
+  static constexpr int NQC = QROWB / 256; // 16-byte q chunks a lane and head
+};
+
 // 16-byte load of streamed K/V data (read once: no reuse to keep in cache).
 __device__ __forceinline__ uint4 ld_stream(const char* p) {
 #if PAGED_DEC_NT
@@ -78,6 +101,16 @@ __device__ __forceinline__ uint4 ld_stream(const char* p) {
   const u32x4_t v = *(const u32x4_t*)p;
 #endif
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 ld_stream8(const char* p) {
+#if PAGED_DEC_NT
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+  return make_uint2(v.x, v.y);
+#else
+  return *(const uint2*)p;
+#endif
 }
 
 template <int CTRL>
@@ -177,30 +210,59 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool BF16>
-__device__ __forceinline__ float dot16(const uint4& q, const uint4& k, float acc) {
-  if constexpr (BF16) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, k.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, k.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, k.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+// Partial dot product of a lane's q chunks with its K chunks (16 lanes a key).
+//   f32:  4 chunks of 4 dims;  bf16: 2 chunks of 8 dims;  e4m3: one chunk of 16 codes against 16 bf16 q dims
+// (two q chunks), the codes widened to bf16 pairs exactly (every e4m3 value is a bf16 value).
+template <int ET>
+__device__ __forceinline__ float qk_dot(const uint4 (&q)[Rows<ET>::NQC], const uint4 (&k)[Rows<ET>::NCQ]) {
+  float acc = 0.f;
+  if constexpr (ET == ET_FP8) {
+    const uint32_t kw[4] = {k[0].x, k[0].y, k[0].z, k[0].w};
+    const uint32_t qw[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x2_t k01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[c], 1.0f, false);
+      const bf16x2_t k23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[c], 1.0f, true);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[2 * c]), k01, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[2 * c + 1]), k23, acc, false);
+    }
   } else {
-    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
-    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
-    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
-    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+#pragma unroll
+    for (int cc = 0; cc < Rows<ET>::NCQ; ++cc) {
+      if constexpr (ET == ET_BF16) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].x), __builtin_bit_cast(bf16x2_t, k[cc].x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].y), __builtin_bit_cast(bf16x2_t, k[cc].y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].z), __builtin_bit_cast(bf16x2_t, k[cc].z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].w), __builtin_bit_cast(bf16x2_t, k[cc].w), acc, false);
+      } else {
+        acc = fmaf(__uint_as_float(q[cc].x), __uint_as_float(k[cc].x), acc);
+        acc = fmaf(__uint_as_float(q[cc].y), __uint_as_float(k[cc].y), acc);
+        acc = fmaf(__uint_as_float(q[cc].z), __uint_as_float(k[cc].z), acc);
+        acc = fmaf(__uint_as_float(q[cc].w), __uint_as_float(k[cc].w), acc);
+      }
+    }
   }
   return acc;
 }
 
-template <bool BF16>
-__device__ __forceinline__ void unpack16(const uint4& v, float* f) {
-  if constexpr (BF16) {
-    f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
-    f[4] = bf16lo(v.z); f[5] = bf16hi(v.z); f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+// The 8 values a lane takes of one V row in PV (32 lanes a key; dims 8*j32 .. 8*j32+7 for bf16 and e4m3,
+// dims 4*j32 + {0..3, 128..131} for float32).  v holds the lane's chunks of the row in load order.
+template <int ET>
+__device__ __forceinline__ void pv_unpack(const uint4& v0, const uint4& v1, float* f) {
+  if constexpr (ET == ET_BF16) {
+    f[0] = bf16lo(v0.x); f[1] = bf16hi(v0.x); f[2] = bf16lo(v0.y); f[3] = bf16hi(v0.y);
+    f[4] = bf16lo(v0.z); f[5] = bf16hi(v0.z); f[6] = bf16lo(v0.w); f[7] = bf16hi(v0.w);
+  } else if constexpr (ET == ET_F32) {
+    f[0] = __uint_as_float(v0.x); f[1] = __uint_as_float(v0.y); f[2] = __uint_as_float(v0.z); f[3] = __uint_as_float(v0.w);
+    f[4] = __uint_as_float(v1.x); f[5] = __uint_as_float(v1.y); f[6] = __uint_as_float(v1.z); f[7] = __uint_as_float(v1.w);
   } else {
-    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    // e4m3: codes in v0.x (dims 0..3) and v0.y (dims 4..7), widened exactly to float32
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v0.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(v0.x, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(v0.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(v0.y, true);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
   }
 }
 
@@ -212,27 +274,31 @@ __device__ __forceinline__ int stream_keys(const DecArgs& a, int s) {
 }
 
 // One 4-key step of loads, the same register footprint for both kinds: a K step (QK, 16 lanes a
-// key) fills x[0 .. NCQ-1]; a V step (PV, 32 lanes a key, two half steps of 2 keys) fills
-// x[NCP*j .. NCP*j + NCP-1] for half step j.
-template <bool BF16>
+// key) fills x[0 .. NCQ-1]; a V step (PV, 32 lanes a key, two half steps of 2 keys) fills half step j's
+// part of x (chunks NCP*j .. NCP*j+NCP-1, or for e4m3 the 8 bytes x[0] words 2j, 2j+1).  For e4m3, ok
+// bit j says that the key of V half step j is real: a masked key's stand-in bytes may hold NaN codes,
+// so its codes are replaced by zeros before they meet its zero probability.
+template <int ET>
 struct StepBuf {
-  static constexpr int NCQ = (HD * (BF16 ? 2 : 4)) / 256;
-  uint4 x[NCQ];
+  uint4 x[Rows<ET>::NCQ];
+  uint32_t ok;
 };
 
-template <bool BF16, int G, int RING>
+template <int ET, int G, int RING>
 __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(DecArgs a) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int ROWB = HD * ES;    // bytes a row
-  constexpr int NCQ = ROWB / 256;  // 16-byte chunks a lane in QK (16 lanes a key)
-  constexpr int NCP = ROWB / 512;  // 16-byte chunks a lane in PV (32 lanes a key)
-  constexpr int EPC = 16 / ES;     // elements a chunk
-  constexpr int NO = NCP * EPC;    // outputs a lane a head (8)
-  constexpr int NSTEP = TILE / 4;  // 4-key steps a tile and phase
-  constexpr int SPT = 2 * NSTEP;   // load steps a tile: NSTEP of K, then NSTEP of V
-  constexpr int DEPTH = RING - 1;       // steps of K/V in flight ahead of the one computed
+  using RT = Rows<ET>;
+  constexpr bool FP8 = ET == ET_FP8;
+  constexpr int ROWB = RT::ROWB;     // bytes a K/V row
+  constexpr int QROWB = RT::QROWB;   // bytes a q row
+  constexpr int NCQ = RT::NCQ;       // 16-byte K chunks a lane in QK
+  constexpr int NQC = RT::NQC;       // 16-byte q chunks a lane and head
+  constexpr int NCP = FP8 ? 1 : ROWB / 512;  // V chunks a lane in PV (e4m3: one 8-byte piece)
+  constexpr int NO = 8;              // outputs a lane a head
+  constexpr int NSTEP = TILE / 4;    // 4-key steps a tile and phase
+  constexpr int SPT = 2 * NSTEP;     // load steps a tile: NSTEP of K, then NSTEP of V
+  constexpr int DEPTH = RING - 1;    // steps of K/V in flight ahead of the one computed
   static_assert(SPT % RING == 0, "ring slots must be compile-time");
-  using Buf = StepBuf<BF16>;
+  using Buf = StepBuf<ET>;
 
   __shared__ int64_t s_keyat[NWAVE][4][TILE];
   __shared__ float s_sc[NWAVE][TILE * G];
@@ -240,6 +306,9 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   __shared__ float s_o[NWAVE][G][HD];
   __shared__ float s_m[NWAVE][G];
   __shared__ float s_l[NWAVE][G];
+  // e4m3 row scales of the keys of the current and the next tile (K, V)
+  __shared__ float s_ks[FP8 ? NWAVE : 1][2][TILE];
+  __shared__ float s_vs[FP8 ? NWAVE : 1][2][TILE];
 
   const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -275,7 +344,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   };
 
   // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
-  const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * ROWB;
+  const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * QROWB;
 
   // Loads of global step gs = SPT * tt + i: i < NSTEP is K step i of tile tt, else V step i - NSTEP.
   // Every load is issued (masked keys and steps past the wave's tiles read the q row instead) so none
@@ -288,22 +357,34 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
       for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream(kp + 256 * cc + 16 * jj);
     } else {
+      b.ok = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t off = s_keyat[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
-        const char* vp = (ok_t && off >= 0) ? a.vb + off : qrow;
+        const bool ok = ok_t && off >= 0;
+        const char* vp = ok ? a.vb + off : qrow;
+        if constexpr (FP8) {
+          const uint2 v = ld_stream8(vp + 8 * j32);
+          if (j == 0) { b.x[0].x = v.x; b.x[0].y = v.y; }
+          else        { b.x[0].z = v.x; b.x[0].w = v.y; }
+          b.ok |= ok ? (1u << j) : 0u;
+        } else {
 #pragma unroll
-        for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
+          for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
+        }
       }
     }
   };
 
-  // q rows of the G query heads of KV head g: 16 dims a lane (chunks at 256*cc + 16*jj).
-  uint4 qr[G][NCQ];
+  // q rows of the G query heads of KV head g: the lane's 16 dims (f32 / bf16: chunks at 256*cc + 16*jj, the
+  // dims its K chunks hold; e4m3 rows: dims 16*jj .. 16*jj+15, bytes 32*jj .. 32*jj+31 of the bf16 row).
+  uint4 qr[G][NQC];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int cc = 0; cc < NCQ; ++cc) qr[h][cc] = *(const uint4*)(qrow + h * ROWB + 256 * cc + 16 * jj);
+    for (int cc = 0; cc < NQC; ++cc)
+      qr[h][cc] = FP8 ? *(const uint4*)(qrow + h * QROWB + 32 * jj + 16 * cc)
+                      : *(const uint4*)(qrow + h * QROWB + 256 * cc + 16 * jj);
 
   float m_run = NEG_INF, l_run = 0.f;  // for head lane % G
   float o[G][NO];
@@ -312,10 +393,21 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < NO; ++e) o[h][e] = 0.f;
 
+  // e4m3: the scales of a key, read through its page (the lookup its row takes); a masked key reads the
+  // region's first scale and gets V scale 0.
+  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, g, pos, 4) : 0; };
+
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
-      s_keyat[w][0][lane] = pos0 >= 0 ? pg_at(a.pg, s, g, pos0, ROWB) : (int64_t)-1;
+      const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
+      s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, g, pos0, ROWB) : (int64_t)-1;
+      if constexpr (FP8) {
+        const int64_t so = scale_off(page0, pos0);
+        const float ks = *(const float*)(a.ksb + so), vs = *(const float*)(a.vsb + so);
+        s_ks[w][0][lane] = ks;
+        s_vs[w][0][lane] = pos0 >= 0 ? vs : 0.f;
+      }
     }
     int id_next = load_id(1);
     wave_lds_sync();
@@ -329,12 +421,25 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
       const int pos1 = key_pos(t + 1, id_next);
       const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
       id_next = load_id(t + 2);
+      float ks1 = 0.f, vs1 = 0.f;
 
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
         if (i == 4) {
           s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, g, pos1, ROWB) : (int64_t)-1;
+          if constexpr (FP8) {
+            const int64_t so = scale_off(page1, pos1);
+            ks1 = *(const float*)(a.ksb + so);
+            vs1 = *(const float*)(a.vsb + so);
+          }
           wave_lds_sync();
+        }
+        if constexpr (FP8) {
+          // tile t+1's scales, stored once their loads have long landed (read from tile t+1 on)
+          if (i == NSTEP + 4) {
+            s_ks[w][(t + 1) & 1][lane] = ks1;
+            s_vs[w][(t + 1) & 1][lane] = pos1 >= 0 ? vs1 : 0.f;
+          }
         }
         if (i == NSTEP) {
           // Online softmax over tile t: lane handles flat entries k*64 + lane (head lane % G).
@@ -353,7 +458,8 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
           for (int k = 0; k < G; ++k) {
             const float p = (ev[k] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[k] - m_new);
-            sc[k * 64 + lane] = p;
+            // the PV weight of key (k*64 + lane) / G carries its V scale; the running sum does not
+            sc[k * 64 + lane] = FP8 ? p * s_vs[w][t & 1][(k * 64 + lane) / G] : p;
             tsum += p;
           }
           tsum = head_sum<G>(tsum);
@@ -379,21 +485,17 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
         if (i < NSTEP) {
           float acc[G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float x = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < NCQ; ++cc) x = dot16<BF16>(qr[h][cc], cur.x[cc], x);
-            acc[h] = x;
-          }
+          for (int h = 0; h < G; ++h) acc[h] = qk_dot<ET>(qr[h], cur.x);
           using R = QkReduce<G>;
           float res[R::NR];
           R::run(acc, res);
           const int kk = 4 * i + grp;
           if ((lane & 3) == 0 && R::writer_row(row)) {
             const bool valid = s_keyat[w][t & 3][kk] >= 0;
+            const float zs = FP8 ? a.zscale * s_ks[w][t & 1][kk] : a.zscale;
 #pragma unroll
             for (int k = 0; k < R::NR; ++k)
-              s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
+              s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * zs : NEG_INF;
           }
         } else {
           const float* pp = s_sc[w];
@@ -401,11 +503,15 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
           for (int j = 0; j < 2; ++j) {
             const int kk = 4 * (i - NSTEP) + 2 * j + half;
             float vf[NO];
-            uint4 vv[NCP];
-#pragma unroll
-            for (int cc = 0; cc < NCP; ++cc) vv[cc] = cur.x[NCP * j + cc];
-#pragma unroll
-            for (int cc = 0; cc < NCP; ++cc) unpack16<BF16>(vv[cc], vf + cc * EPC);
+            if constexpr (FP8) {
+              const bool ok = (cur.ok >> j) & 1u;
+              uint4 v = {0u, 0u, 0u, 0u};
+              v.x = ok ? (j == 0 ? cur.x[0].x : cur.x[0].z) : 0u;
+              v.y = ok ? (j == 0 ? cur.x[0].y : cur.x[0].w) : 0u;
+              pv_unpack<ET>(v, v, vf);
+            } else {
+              pv_unpack<ET>(cur.x[NCP * j], cur.x[NCP * j + NCP - 1], vf);
+            }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               const float p = pp[kk * G + h];
@@ -430,10 +536,10 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int cc = 0; cc < NCP; ++cc) {
-        const int e0 = (512 * cc + 16 * j32) / ES;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s_o[w][h][e0 + e] = o[h][cc * EPC + e];
+      for (int e = 0; e < NO; ++e) {
+        // f32: dims 4*j32 + {0..3} and 128 + 4*j32 + {0..3}; bf16 / e4m3: dims 8*j32 + e
+        const int d = ET == ET_F32 ? (e < 4 ? 4 * j32 + e : 128 + 4 * j32 + e - 4) : 8 * j32 + e;
+        s_o[w][h][d] = o[h][e];
       }
   }
   if (lane < G) {
@@ -520,25 +626,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 
 // Ring depth: one step ahead keeps the register file small for long streams, where every wave has
 // several tiles and two waves share a SIMD; streams of at most two tiles a wave (short or sparse
-// key lists) run their few steps three ahead instead.  The depth changes only when loads are
-// issued, never the arithmetic, so results do not depend on it.
-template <bool BF16, int G>
+// key lists) run their few steps three ahead instead.  e4m3 steps carry half the bytes of bf16
+// steps, so they keep more steps in flight.  The depth changes only when loads are issued, never
+// the arithmetic, so results do not depend on it.
+template <int ET, int G>
 hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv, n_streams);
   const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
   const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
-  if constexpr (BF16) {
+  if constexpr (ET == ET_BF16) {
     if (short_keys)
-      hipLaunchKernelGGL((decode_split_kernel<true, G, PAGED_DEC_RING_SHORT>), grid, dim3(WGS), 0, st, a);
+      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_SHORT>), grid, dim3(WGS), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<true, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
+      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
+  } else if constexpr (ET == ET_FP8) {
+    if (short_keys)
+      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_FP8_SHORT>), grid, dim3(WGS), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_FP8>), grid, dim3(WGS), 0, st, a);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<false, G, 2>), grid, dim3(WGS), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<ET, G, 2>), grid, dim3(WGS), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq, n_streams), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int ET>
+hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_t<ET, 1>(a, n_streams, st);
+    case 2: return launch_t<ET, 2>(a, n_streams, st);
+    case 4: return launch_t<ET, 4>(a, n_streams, st);
+    case 8: return launch_t<ET, 8>(a, n_streams, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -549,22 +672,12 @@ int dec_splits_max(int max_keys) {
   return a < MAX_SPLITS ? a : MAX_SPLITS;
 }
 
-hipError_t launch_decode(const DecArgs& a, bool bf16, int G, int n_streams, hipStream_t st) {
+hipError_t launch_decode(const DecArgs& a, int elem, int G, int n_streams, hipStream_t st) {
   if (n_streams <= 0) return hipSuccess;
-  if (bf16) {
-    switch (G) {
-      case 1: return launch_t<true, 1>(a, n_streams, st);
-      case 2: return launch_t<true, 2>(a, n_streams, st);
-      case 4: return launch_t<true, 4>(a, n_streams, st);
-      case 8: return launch_t<true, 8>(a, n_streams, st);
-    }
-  } else {
-    switch (G) {
-      case 1: return launch_t<false, 1>(a, n_streams, st);
-      case 2: return launch_t<false, 2>(a, n_streams, st);
-      case 4: return launch_t<false, 4>(a, n_streams, st);
-      case 8: return launch_t<false, 8>(a, n_streams, st);
-    }
+  switch (elem) {
+    case ET_F32: return launch_g<ET_F32>(a, G, n_streams, st);
+    case ET_BF16: return launch_g<ET_BF16>(a, G, n_streams, st);
+    case ET_FP8: return launch_g<ET_FP8>(a, G, n_streams, st);
   }
   return hipErrorInvalidValue;
 }

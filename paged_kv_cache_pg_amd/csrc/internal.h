@@ -15,6 +15,8 @@ struct DecArgs {
   const void* q;          // [S][Hq][HD]
   const char* kb;         // K region base
   const char* vb;         // V region base
+  const char* ksb;        // e4m3 rows: K scale region base ([H][ptok] float32 a page)
+  const char* vsb;        // e4m3 rows: V scale region base
   PgDev pg;
   const int32_t* lens;    // dense: lengths [S]; sparse: selected block counts [S]
   const int32_t* ids;     // sparse: block ids [S][ids_stride]; dense: nullptr
@@ -30,7 +32,8 @@ struct DecArgs {
 };
 
 int dec_splits_max(int max_keys);
-hipError_t launch_decode(const DecArgs& a, bool bf16, int G, int n_streams, hipStream_t st);
+// elem: 0 float32, 1 bf16, 2 e4m3 codes with a float32 scale a row (q bf16)
+hipError_t launch_decode(const DecArgs& a, int elem, int G, int n_streams, hipStream_t st);
 
 // ---- prefill (prefill.hip) ------------------------------------------------
 struct PreArgs {
@@ -102,6 +105,8 @@ struct AppendArgs {
   char* vb;
   char* ikb;
   char* pooled;
+  char* ksb;              // e4m3 arenas: K and V scale region bases
+  char* vsb;
   PgDev pg;               // page_bytes of the arena
   const int32_t* pos0;    // [S] position of each stream's first new token
   int32_t n;              // new tokens a stream
@@ -110,7 +115,8 @@ struct AppendArgs {
   int32_t ik_row_bytes;   // indexer-key row (0: none)
   int32_t idx_dim;
   int32_t max_len;
-  int32_t bf16;           // arena element type
+  int32_t bf16;           // arena element type: bf16 (else float32) ...
+  int32_t fp8;            // ... or e4m3 codes with a float32 scale a row (bf16 step rows, no indexer keys)
 };
 hipError_t launch_append(const AppendArgs& a, int n_streams, hipStream_t st);
 

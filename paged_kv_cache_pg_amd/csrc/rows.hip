@@ -115,6 +115,74 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// e4m3 code of y (OCP E4M3 from its definition: bias 7, 3 mantissa bits, subnormal step 2^-9):
+// the nearest code, ties to the even code, magnitudes past the largest finite value (448) held
+// at 448, the sign bit kept.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float m = fminf(fabsf(y), 448.f);
+  uint32_t mag;
+  if (m < 0.015625f) {
+    // below the smallest normal 2^-6 the codes step by 2^-9; 8 steps reach code 0x08 = 2^-6
+    mag = (uint32_t)__builtin_rintf(m * 512.f);
+  } else {
+    // keep 3 of float32's 23 mantissa bits, round half to even (a carry moves into the exponent),
+    // then move the exponent bias from 127 to 7
+    const uint32_t b = __float_as_uint(m);
+    mag = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | mag;
+}
+
+// e4m3 store of a step's K and V rows (PR #1170 commit 5c09685: the fp8 store takes a row's codes and
+// fp32 scale through the page table).  A bf16 row x becomes scale = amax / 448 and codes
+// e4m3(x / scale) (amax = max |x|; float32 quotients, correctly rounded); a row of zeros gets scale 0
+// and zero codes.  Item = (token, K or V, head) row; 16 lanes a row, 16 dims (one 16-byte code chunk)
+// a lane.
+__global__ __launch_bounds__(256) void append8_kernel(AppendArgs a) {
+  const int s = blockIdx.y;
+  const int p0 = min(max(a.pos0[s], 0), a.max_len);
+  const int nn = max(0, min(a.n, a.max_len - p0));
+  if (nn == 0) return;
+  const int64_t rows = (int64_t)nn * 2 * a.hkv;
+  const int l = threadIdx.x & 15;
+  for (int64_t r0 = (int64_t)blockIdx.x * 16; r0 < rows; r0 += (int64_t)gridDim.x * 16) {
+    const int64_t r = r0 + (threadIdx.x >> 4);  // the same for the 16 lanes of a row
+    if (r < rows) {
+      const int t = (int)(r / (2 * a.hkv));
+      const int rem = (int)(r - (int64_t)t * 2 * a.hkv);
+      const int v = rem >= a.hkv;
+      const int h = rem - v * a.hkv;
+      const int p = p0 + t;
+      const char* src = (v ? a.v_new : a.k_new) + (((int64_t)s * a.n + t) * a.hkv + h) * (HD * 2) + 32 * l;
+      const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 16);
+      const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[2 * k] = bf16lo(wv[k]);
+        x[2 * k + 1] = bf16hi(wv[k]);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const float scale = amax / 448.f;
+      uint32_t cw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= (amax > 0.f ? e4m3_code(x[4 * k + e] / scale) : 0u) << (8 * e);
+        cw[k] = w;
+      }
+      *(uint4*)((v ? a.vb : a.kb) + pg_at(a.pg, s, h, p, HD) + 16 * l) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      if (l == 0) *(float*)((v ? a.vsb : a.ksb) + pg_at(a.pg, s, h, p, 4)) = scale;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, int n_streams, hipStream_t st) {
@@ -124,7 +192,12 @@ hipError_t launch_append(const AppendArgs& a, int n_streams, hipStream_t st) {
   int gx = (int)((items + 255) / 256);
   if (gx > 4096) gx = 4096;
   if (gx < 1) gx = 1;
-  if (a.bf16) hipLaunchKernelGGL(append_kernel<true>, dim3(gx, n_streams), dim3(256), 0, st, a);
+  if (a.fp8) {
+    const int64_t rows = (int64_t)a.n * 2 * a.hkv;
+    int g8 = (int)((rows + 15) / 16);
+    if (g8 > 4096) g8 = 4096;
+    hipLaunchKernelGGL(append8_kernel, dim3(g8, n_streams), dim3(256), 0, st, a);
+  } else if (a.bf16) hipLaunchKernelGGL(append_kernel<true>, dim3(gx, n_streams), dim3(256), 0, st, a);
   else hipLaunchKernelGGL(append_kernel<false>, dim3(gx, n_streams), dim3(256), 0, st, a);
   return hipGetLastError();
 }

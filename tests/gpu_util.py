@@ -99,3 +99,47 @@ def rel_err_rows(x: np.ndarray, ref: np.ndarray) -> float:
     den = np.max(np.abs(r), axis=1)
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den)) if len(num) else 0.0
+
+
+class PlacedFp8:
+    """e4m3 rows and their scales placed by the oracle in one arena (paged through a table, or contiguously)."""
+
+    def __init__(self, lens, n_kv_heads, page_pos, KC, VC, KS, VS, table=None, n_pages=None, guard: int = 4096):
+        self.lens_list = [int(x) for x in lens]
+        cap = max(self.lens_list + [1])
+        self.paged = table is not None
+        self.page_pos = page_pos if self.paged else max(cap, KC.shape[2])
+        self.table_np = table
+        self.olay = O.PageLayout(n_kv_heads, 256, self.page_pos, "fp8")
+        self.lay = P.ArenaLayout(n_kv_heads, 256, self.page_pos, P.PAGED_FP8_E4M3)
+        assert self.lay.page_bytes == self.olay.page_bytes and self.lay.ks_off == self.olay.ks_off
+        n_pages = n_pages if self.paged else len(self.lens_list)
+        arena = O.place_fp8(self.olay, table, n_pages, self.lens_list, KC, VC, KS, VS)
+        self.arena_np = arena
+        self.guard = guard
+        self.buf = dev(np.concatenate([np.full(guard, 0xA5, np.uint8), arena, np.full(guard, 0xA5, np.uint8)]))
+        self.base = self.buf.data_ptr() + guard
+        self.table = dev(table.astype(np.int32)) if self.paged else None
+        self.pg = P.make_pg(self.table, self.page_pos, self.lay.page_elems)
+        self.kv = P.make_kv(self.base + self.lay.k_off, self.base + self.lay.v_off, P.PAGED_FP8_E4M3, n_kv_heads,
+                            256, self.base + self.lay.ks_off, self.base + self.lay.vs_off)
+        self.lens = dev(np.array(self.lens_list, np.int32))
+
+    def arena_now(self) -> np.ndarray:
+        b = host_bytes(self.buf)
+        return b[self.guard:len(b) - self.guard]
+
+    def guards_intact(self) -> bool:
+        b = host_bytes(self.buf)
+        return bool(np.all(b[:self.guard] == 0xA5) and np.all(b[len(b) - self.guard:] == 0xA5))
+
+
+def decode_fp8(pl: PlacedFp8, q: torch.Tensor, n_q_heads: int, scale: float, max_len=None, out=None):
+    S = len(pl.lens_list)
+    max_len = max_len if max_len is not None else max(pl.lens_list + [0])
+    ws_bytes = P.paged_attn_decode_workspace(S, n_q_heads, max_len)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    if out is None:
+        out = torch.empty((S, n_q_heads, 256), dtype=torch.float32, device="cuda")
+    P.paged_attn_decode(q, P.PAGED_BF16, n_q_heads, pl.kv, pl.pg, pl.lens, S, max_len, scale, out, ws)
+    return out

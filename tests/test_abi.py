@@ -153,3 +153,27 @@ def test_prefill_refusals():
     assert L.paged_attn_prefill(FAKE, 1, -1, 0, 32, ctypes.byref(kv), ctypes.byref(pg), 1, 0.0625, FAKE, 0, 0, 0) == E
     assert L.paged_attn_prefill(MIS, 1, 2048, 0, 32, ctypes.byref(kv), ctypes.byref(pg), 1, 0.0625, FAKE, 0, 0,
                                 0) == E
+
+
+def test_fp8_refusals():
+    E, U = B.PAGED_EINVAL, B.PAGED_EUNSUPPORTED
+    L = B.lib()
+    F8 = B.PAGED_FP8_E4M3
+
+    def kv8(ks=FAKE, vs=FAKE):
+        return B.make_kv(FAKE, FAKE, F8, 4, 256, ks, vs)
+
+    pg8 = _pg(pe=4 * 256 * 256 * 2 + 2 * 4 * 256 * 4)       # e4m3 page: bytes
+    assert _decode(kv=kv8(), pg=pg8, qd=B.PAGED_F32) == U   # e4m3 rows take bf16 queries
+    assert _decode(kv=kv8(), pg=pg8, qd=F8) == E            # e4m3 is no query type
+    assert _decode(kv=kv8(ks=0), pg=pg8) == E               # scale regions are required
+    assert _decode(kv=kv8(vs=FAKE + 2), pg=pg8) == E        # and 4-byte aligned
+    assert _decode(kv=kv8(), pg=_pg(pe=4 * 256 * 256 - 16)) == E   # codes of a page do not fit
+    assert L.paged_attn_prefill(FAKE, 1, 16, 0, 32, ctypes.byref(kv8()), ctypes.byref(pg8), 1, 0.0625, FAKE, 0, 0,
+                                0) == U
+    # the e4m3 store keeps no indexer keys
+    assert L.paged_kv_append(FAKE, FAKE, FAKE, 1, ctypes.byref(kv8()), FAKE, FAKE, 128, ctypes.byref(pg8), FAKE, 4,
+                             40960, 0) == U
+    # indexer-key, pooled and copied rows are never e4m3
+    assert L.paged_pool_blocks(FAKE, FAKE, 128, F8, ctypes.byref(pg8), FAKE, FAKE, 3, 131072, 0) == E
+    assert L.paged_rows_store(FAKE, 0, 0, 256, FAKE, 4, 256, F8, ctypes.byref(pg8), FAKE, FAKE, 1, 160, 0) == E
