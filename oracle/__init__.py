@@ -11,6 +11,7 @@ from .paged_oracle import (  # noqa: F401
     gather,
     read_pooled,
     decode,
+    decode_window,
     prefill,
     sparse,
     pool,

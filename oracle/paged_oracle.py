@@ -21,6 +21,8 @@ Parity status per function:
       round trip, red controls)
   decode / prefill / sparse                 : pinned (closed forms, invariants,
       50-digit brute force on tiny shapes)
+  decode_window                             : pinned (closed form, equality with the
+      causal prefill and with decode, 50-digit brute force)
   pool                                      : pinned (closed forms, exact quarters)
   scores                                    : pinned (exact integer scores,
       one-hot rows, linearity)
@@ -249,6 +251,33 @@ def decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, lens: Sequence[int], sca
             g = h // G
             z = scale * (K[s, g, :L] @ q[s, h])
             out[s, h] = _softmax_rows_attend(z[None, :], V[s, g, :L])[0]
+    return out
+
+
+def decode_window(q: np.ndarray, K: np.ndarray, V: np.ndarray, lens: Sequence[int], scale: float) -> np.ndarray:
+    """Decode of a window of W query tokens at the end of each stream's cache, float64.
+
+    q [S][W][Hq][D], K/V [S][Hkv][cap][D].  Query w of stream s stands at
+    position L - W + w and attends to keys 0 .. L - W + w; a query with no key
+    (L - W + w < 0) gives a zero row.  [P1 "What this changes"] names
+    fn_attn_chunks_ahead beside fn_attn_chunks and nothing more: the reading is
+    the drafted-token form of decode, several new tokens verified at once, each
+    seeing the cache up to itself.
+    """
+    S, W, Hq, D = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((S, W, Hq, D), dtype=np.float64)
+    for s in range(S):
+        L = int(lens[s])
+        for w in range(W):
+            last = L - W + w          # the query's own position
+            if last < 0:
+                continue
+            for h in range(Hq):
+                g = h // G
+                z = scale * (K[s, g, :last + 1] @ q[s, w, h])
+                out[s, w, h] = _softmax_rows_attend(z[None, :], V[s, g, :last + 1])[0]
     return out
 
 

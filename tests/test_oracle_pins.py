@@ -345,3 +345,51 @@ def test_oracle_matches_its_stored_small_case():
             assert all(np.array_equal(np.array(x), np.array(y)) for x, y in zip(a, b)), key
         else:
             assert np.allclose(np.array(a), np.array(b), rtol=0, atol=1e-14), key
+
+
+# ----------------------------------------------------------------------------
+# Windowed decode (fn_attn_chunks_ahead, PR #1169: W queries at the end of the cache)
+# ----------------------------------------------------------------------------
+
+def test_decode_window_closed_form_and_short_streams():
+    S, W, Hq, Hkv, D, cap = 2, 3, 4, 2, 8, 10
+    q = _rand((S, W, Hq, D), 70)
+    Ke = np.ones((S, Hkv, cap, D))
+    Vp = np.broadcast_to(np.arange(cap, dtype=np.float64)[None, None, :, None], (S, Hkv, cap, D)).copy()
+    out = O.decode_window(q, Ke, Vp, [10, 2], 0.3)
+    # equal keys: query w of a stream of length L averages positions 0 .. L - W + w
+    for w in range(W):
+        assert np.allclose(out[0, w], (10 - W + w) / 2, atol=1e-13)
+    # L = 2 < W = 3: query 0 stands at position -1 and sees nothing
+    assert np.array_equal(out[1, 0], np.zeros((Hq, D)))
+    assert np.allclose(out[1, 1], 0.0, atol=1e-13) and np.allclose(out[1, 2], 0.5, atol=1e-13)
+
+
+def test_decode_window_equals_causal_prefill_and_decode():
+    S, W, Hq, Hkv, D, cap = 2, 4, 8, 2, 16, 40
+    q, K, V = _rand((S, W, Hq, D), 71), _rand((S, Hkv, cap, D), 72), _rand((S, Hkv, cap, D), 73)
+    lens = [40, 17]
+    out = O.decode_window(q, K, V, lens, 0.25)
+    for s, L in enumerate(lens):
+        pre = O.prefill(q[s], K[s], V[s], L - W, 0.25, causal=True)
+        assert np.allclose(out[s], pre, atol=1e-14)
+        last = O.decode(q[s:s + 1, W - 1], K[s:s + 1], V[s:s + 1], [L], 0.25)[0]
+        assert np.allclose(out[s, W - 1], last, atol=1e-14)
+
+
+def test_decode_window_matches_50_digit_brute_force():
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    W, Hq, Hkv, D, L = 2, 2, 1, 4, 5
+    q, K, V = _rand((1, W, Hq, D), 74), _rand((1, Hkv, L, D), 75), _rand((1, Hkv, L, D), 76)
+    out = O.decode_window(q, K, V, [L], 0.5)
+    for w in range(W):
+        n = L - W + w + 1
+        for h in range(Hq):
+            z = [mp.mpf(0.5) * mp.fsum(mp.mpf(q[0, w, h, d]) * mp.mpf(K[0, 0, j, d]) for d in range(D))
+                 for j in range(n)]
+            e = [mp.exp(x) for x in z]
+            tot = mp.fsum(e)
+            for d in range(D):
+                ref = mp.fsum(e[j] * mp.mpf(V[0, 0, j, d]) for j in range(n)) / tot
+                assert abs(float(ref) - out[0, w, h, d]) <= 1e-13 * max(1.0, abs(float(ref)))
