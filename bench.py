@@ -301,33 +301,123 @@ class SparseBench:
         return ok, err
 
 
+class DecodeFp8Bench:
+    """The decode workload with e4m3 rows (a float32 scale a row): 4 streams x 40960 positions, pages of 256
+    shuffled in one arena, 32 q / 4 KV heads, head dim 256, bf16 q.  The rows are N(0,1) bf16 drawn on the
+    device from a seeded generator and written by the library's own e4m3 store (paged_kv_append), through
+    the table, so the arena holds what a serving loop would have stored."""
+    S, L, PTOK, HQ, HKV, D = 4, 40960, 256, 32, 4, 256
+    CHUNK = 4096
+
+    def __init__(self, seed: int = 7):
+        import numpy as np
+        import torch
+        import paged_kv_cache_pg_amd as P
+        from paged_kv_cache_pg_amd.inputs import make_table
+        self.P, self.torch, self.np = P, torch, np
+        S, L = self.S, self.L
+        rng = np.random.default_rng(seed)
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        self.table_np, n_pages = make_table("shuffled", [L // self.PTOK] * S, rng)
+        self.lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_FP8_E4M3)
+        self.table = torch.from_numpy(self.table_np.astype(np.int32)).cuda()
+        self.pg = P.make_pg(self.table, self.PTOK, self.lay.page_elems)
+        self.q = torch.randn((S, self.HQ, self.D), generator=gen, device="cuda").to(torch.bfloat16)
+        self.lens = torch.full((S,), L, dtype=torch.int32, device="cuda")
+        self.arenas, self.kvs = [], []
+        for copy in range(2):
+            arena = torch.zeros(n_pages * self.lay.page_bytes, dtype=torch.uint8, device="cuda")
+            b = arena.data_ptr()
+            kv = P.make_kv(b + self.lay.k_off, b + self.lay.v_off, P.PAGED_FP8_E4M3, self.HKV, self.D,
+                           b + self.lay.ks_off, b + self.lay.vs_off)
+            for p0 in range(0, L, self.CHUNK):
+                shape = (S, self.CHUNK, self.HKV, self.D)
+                k_new = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+                v_new = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+                pos0 = torch.full((S,), p0, dtype=torch.int32, device="cuda")
+                P.paged_kv_append(k_new, v_new, None, self.CHUNK, kv, None, None, 0, self.pg, pos0, S, L)
+                torch.cuda.synchronize()
+            self.arenas.append(arena)
+            self.kvs.append(kv)
+        self.ws = torch.zeros(P.paged_attn_decode_workspace(S, self.HQ, L), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((S, self.HQ, self.D), dtype=torch.float32, device="cuda")
+        self.alg_bytes = (S * self.HKV * L * (self.D + 4) * 2          # K and V codes and scales
+                          + self.q.numel() * 2 + S * self.table_np.shape[1] * 4 + S * 4 + self.out.numel() * 4)
+
+    def step(self, i: int):
+        self.P.paged_attn_decode(self.q, self.P.PAGED_BF16, self.HQ, self.kvs[i & 1], self.pg, self.lens, self.S,
+                                 self.L, 1 / 16, self.out, self.ws)
+
+    def check(self):
+        """Sampled rows against the oracle over the stored codes x scales (outside the timed region)."""
+        import oracle as O
+        np, torch = self.np, self.torch
+        self.step(0)
+        torch.cuda.synchronize()
+        out = self.out.cpu().numpy()
+        arena = self.arenas[0].cpu().numpy()
+        q = self.q.float().cpu().numpy().astype(np.float64)
+        lay = O.PageLayout(self.HKV, self.D, self.PTOK, "fp8")
+        worst = 0.0
+        for s, h in [(0, 0), (3, 31)]:
+            g = h // (self.HQ // self.HKV)
+            kc = np.empty((self.L, self.D), np.uint8)
+            vc = np.empty_like(kc)
+            ks = np.empty(self.L, np.float32)
+            vs = np.empty_like(ks)
+            for lp in range(self.L // self.PTOK):
+                p0 = lp * self.PTOK
+                o = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, self.D)
+                so = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, 4)
+                kc[p0:p0 + self.PTOK] = arena[lay.k_off + o:lay.k_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
+                vc[p0:p0 + self.PTOK] = arena[lay.v_off + o:lay.v_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
+                ks[p0:p0 + self.PTOK] = arena[lay.ks_off + so:lay.ks_off + so + self.PTOK * 4].view(np.float32)
+                vs[p0:p0 + self.PTOK] = arena[lay.vs_off + so:lay.vs_off + so + self.PTOK * 4].view(np.float32)
+            ref = O.decode(q[s:s + 1, h:h + 1], O.e4m3_dequantize(kc, ks)[None, None],
+                           O.e4m3_dequantize(vc, vs)[None, None], [self.L], 1 / 16)[0, 0]
+            worst = max(worst, float(np.max(np.abs(out[s, h] - ref)) / np.max(np.abs(ref))))
+        return worst
+
+
 class AppendBench:
     """paged_kv_append into pages of 256 (shuffled), 4 KV heads, head dim 256, 128-wide indexer keys, bf16:
     a decode step (4 streams x 1 token at position 4095, which completes a block of four) and a prefill chunk
-    (1 stream x 2048 tokens at position 2048)."""
+    (1 stream x 2048 tokens at position 2048).  With fp8, the same steps into an e4m3 arena (bf16 rows in,
+    codes and a float32 scale a row out, no indexer keys)."""
     HKV, D, DI, PTOK = 4, 256, 128, 256
 
-    def __init__(self, n_streams: int, n_new: int, pos0: int, seed: int = 6):
+    def __init__(self, n_streams: int, n_new: int, pos0: int, seed: int = 6, fp8: bool = False):
         import numpy as np
         import torch
         import paged_kv_cache_pg_amd as P
         from paged_kv_cache_pg_amd.inputs import make_table
         self.P, self.torch = P, torch
         S, L = n_streams, pos0 + n_new
-        lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_BF16, idx_dim=self.DI)
+        self.fp8 = fp8
+        if fp8:
+            lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_FP8_E4M3)
+        else:
+            lay = P.ArenaLayout(self.HKV, self.D, self.PTOK, P.PAGED_BF16, idx_dim=self.DI)
         rng = np.random.default_rng(seed)
         table, n_pages = make_table("shuffled", [(L + self.PTOK - 1) // self.PTOK] * S, rng)
         self.table = torch.from_numpy(table.astype(np.int32)).cuda()
         self.pg = P.make_pg(self.table, self.PTOK, lay.page_elems)
         self.arena = torch.zeros(n_pages * lay.page_bytes, dtype=torch.uint8, device="cuda")
         base = self.arena.data_ptr()
-        self.kv = P.make_kv(base + lay.k_off, base + lay.v_off, P.PAGED_BF16, self.HKV, self.D)
-        self.ik, self.pooled = base + lay.ik_off, base + lay.pool_off
         self.k_new = torch.randn((S, n_new, self.HKV, self.D), device="cuda").to(torch.bfloat16)
         self.v_new = torch.randn((S, n_new, self.HKV, self.D), device="cuda").to(torch.bfloat16)
-        self.ik_new = torch.randn((S, n_new, self.DI), device="cuda").to(torch.bfloat16)
         self.pos0 = torch.full((S,), pos0, dtype=torch.int32, device="cuda")
         self.S, self.n, self.L = S, n_new, L
+        if fp8:
+            self.kv = P.make_kv(base + lay.k_off, base + lay.v_off, P.PAGED_FP8_E4M3, self.HKV, self.D,
+                                base + lay.ks_off, base + lay.vs_off)
+            self.ik = self.pooled = self.ik_new = None
+            # bf16 K and V rows read once, codes and scales written once
+            self.bytes = S * n_new * 2 * self.HKV * (self.D * 2 + self.D + 4)
+            return
+        self.kv = P.make_kv(base + lay.k_off, base + lay.v_off, P.PAGED_BF16, self.HKV, self.D)
+        self.ik, self.pooled = base + lay.ik_off, base + lay.pool_off
+        self.ik_new = torch.randn((S, n_new, self.DI), device="cuda").to(torch.bfloat16)
         n_blocks = S * ((pos0 + n_new) // 4 - pos0 // 4)
         # K, V and indexer-key rows read and written once, pooled rows written once
         self.bytes = 2 * S * n_new * (2 * self.HKV * self.D * 2 + self.DI * 2) + n_blocks * self.DI * 4
@@ -365,8 +455,11 @@ def time_graph(fn, steps: int, warmup: int):
 
 def run_append(args):
     out = {}
-    for name, (S, n, p0) in (("decode_step_4x1", (4, 1, 4095)), ("prefill_chunk_1x2048", (1, 2048, 2048))):
-        ab = AppendBench(S, n, p0)
+    for name, (S, n, p0, fp8) in (("decode_step_4x1", (4, 1, 4095, False)),
+                                  ("prefill_chunk_1x2048", (1, 2048, 2048, False)),
+                                  ("decode_step_4x1_e4m3", (4, 1, 4095, True)),
+                                  ("prefill_chunk_1x2048_e4m3", (1, 2048, 2048, True))):
+        ab = AppendBench(S, n, p0, fp8=fp8)
         ms = time_graph(ab.step, args.steps, args.warmup)
         out[name] = {"us": round(ms * 1e3, 2), "bytes": ab.bytes, "GB_per_s": round(ab.bytes / (ms * 1e-3) / 1e9, 1)}
         log(f"append {name}: {ms * 1e3:.1f} us, {ab.bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
@@ -411,6 +504,26 @@ def time_launches(fn, n: int):
     return sum(per) / n, per[0], per[n // 2]
 
 
+def run_window(dec, args, W: int = 2):
+    """The decode workload with a window of W queries a stream (drafted tokens verified at once): K/V
+    are read once for all W queries."""
+    import torch
+    P = dec.P
+    q = torch.randn((dec.S, W, dec.HQ, dec.D), device="cuda").to(torch.bfloat16)
+    ws = torch.zeros(P.paged_attn_decode_window_workspace(dec.S, dec.HQ, W, dec.L), dtype=torch.uint8, device="cuda")
+    out = torch.empty((dec.S, W, dec.HQ, dec.D), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        P.paged_attn_decode_window(q, P.PAGED_BF16, dec.HQ, W, dec.kvs[i & 1], dec.pg, dec.lens, dec.S, dec.L, 1 / 16,
+                                   out, ws)
+    ms, _ = time_steps(step, args.steps, args.warmup)
+    nbytes = dec.alg_bytes + dec.q.numel() * 2 * (W - 1) + dec.out.numel() * 4 * (W - 1)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode window {W}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s, {dec.S * W / (ms * 1e-3):.0f} tokens/s")
+    return {"window": W, "us_per_step": round(ms * 1e3, 2), "alg_bytes": nbytes, "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_per_s": round(dec.S * W / (ms * 1e-3), 1)}
+
+
 def run_decode(args):
     dec = DecodeBench()
     ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
@@ -430,7 +543,25 @@ def run_decode(args):
                      "avg_launch_us": round(ms_call * 1e3, 2), "min_launch_us": round(ms_min * 1e3, 2),
                      "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
+        "decode_window": run_window(dec, args),
     }
+    del dec
+    return out
+
+
+def run_decode_fp8(args):
+    dec = DecodeFp8Bench()
+    ms_step, _ = time_steps(dec.step, args.steps, args.warmup)
+    ms_call, ms_min, ms_med = time_launches(dec.step, max(args.steps, 20))
+    err = dec.check()
+    gbs = dec.alg_bytes / (ms_step * 1e-3) / 1e9
+    call_gbs = dec.alg_bytes / (ms_call * 1e-3) / 1e9
+    log(f"decode e4m3: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s ({call_gbs / HBM_PEAK_GBS:.1%} of HBM peak a "
+        f"launch); sampled rows within {err:.2e} of the oracle")
+    out = {"us_per_step": round(ms_step * 1e3, 2), "GB_per_s": round(gbs, 1), "alg_bytes_per_launch": dec.alg_bytes,
+           "avg_launch_us": round(ms_call * 1e3, 2), "median_launch_us": round(ms_med * 1e3, 2),
+           "hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4), "oracle_max_rel_err": err,
+           "tokens_per_s": round(dec.S / (ms_step * 1e-3), 1)}
     del dec
     return out
 
@@ -479,7 +610,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "sparse", "append"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode_fp8", "prefill", "sparse", "append"], default=None,
                     help="run one row only (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -508,6 +639,9 @@ def main():
     }
     if args.only in (None, "decode"):
         result.update(run_decode(args))
+        torch.cuda.empty_cache()
+    if args.only in (None, "decode_fp8"):
+        result["decode_e4m3"] = run_decode_fp8(args)
         torch.cuda.empty_cache()
     if args.only in (None, "prefill"):
         result["prefill"] = run_prefill(args)

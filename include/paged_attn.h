@@ -133,6 +133,31 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
 size_t paged_attn_decode_workspace(int32_t n_streams, int32_t n_q_heads, int32_t max_len);
 
 /* ------------------------------------------------------------------------ */
+/* Windowed decode ([P1 "What this changes" names fn_attn_chunks_ahead beside
+ * fn_attn_chunks; the reading taken: the form that verifies drafted tokens,
+ * a window of queries at the end of each stream's cache, read through pg_at
+ * like decode).
+ *
+ * Query w (0 <= w < n_window) of stream s stands at position L_s - n_window + w
+ * (L_s = seq_lens[s] clamped to [0, max_len]; the window's rows are already
+ * stored) and attends, per head, to keys 0 .. L_s - n_window + w; a query
+ * with no key gets a zero row.  n_window = 1 is paged_attn_decode.
+ *   q        device [n_streams][n_window][n_q_heads][256] bf16, 16-byte aligned
+ *   out      device [n_streams][n_window][n_q_heads][256] float32
+ *   workspace >= paged_attn_decode_window_workspace(n_streams, n_q_heads, n_window, max_len)
+ *            bytes, as for decode
+ * Serves BF16 and FP8_E4M3 rows, n_window 1 .. 4 with n_window * (n_q_heads / n_kv_heads) <= 16
+ * (PAGED_EUNSUPPORTED otherwise).
+ */
+int paged_attn_decode_window(const void *q, int32_t q_dtype, int32_t n_q_heads, int32_t n_window,
+                             const paged_kv *kv, const paged_pg *pg,
+                             const int32_t *seq_lens, int32_t n_streams, int32_t max_len,
+                             float scale, float *out,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t paged_attn_decode_window_workspace(int32_t n_streams, int32_t n_q_heads, int32_t n_window,
+                                          int32_t max_len);
+
+/* ------------------------------------------------------------------------ */
 /* Chunked causal prefill for one stream ([P2 maintainer reply: paged or mixed
  * prompt batches take the page-run path, flat ones the tensor-core attention;
  * here one MFMA kernel serves both through pg_at]).
@@ -249,13 +274,22 @@ int paged_rows_gather(void *dst, int64_t stride_s, int64_t stride_h, int64_t str
  * float32(((IK[4b] + IK[4b+1]) + IK[4b+2]) + IK[4b+3]) / 4) (float64 sum), the value
  * paged_pool_blocks writes: rows before pos0[s] are read from the arena (stored by
  * earlier steps), the new ones from ik_new.  One launch.
- *   k_new, v_new device [n_streams][n_new][n_kv_heads][head_dim], kv->dtype, 16-byte aligned
+ *   k_new, v_new device [n_streams][n_new][n_kv_heads][head_dim], kv->dtype (bf16 for e4m3 arenas),
+ *                16-byte aligned
  *   ik_new       device [n_streams][n_new][idx_dim] of kv->dtype, or NULL (no indexer keys:
  *                ik, pooled and idx_dim are ignored)
  *   kv           K and V region bases; ik, pooled: region bases as for paged_pool_blocks
  *   pos0         device [n_streams] int32
  * page_pos must be a multiple of 4 when ik_new is given.  The caller must not run two
  * appends that write the same rows concurrently.
+ *
+ * e4m3 arenas (kv->dtype == PAGED_FP8_E4M3, [P2 commit 5c09685]: the fp8 store takes a row's
+ * codes and fp32 scale through the table): k_new and v_new are bf16 and every (token, head) row x
+ * is stored as scale = amax / 448 (amax = max |x|) in the scale regions and codes e4m3(x / scale)
+ * in the code regions, both quotients float32 and correctly rounded, e4m3() the nearest code with
+ * ties to the even code, magnitudes beyond 448 held at 448 and the sign bit kept; a row of zeros
+ * stores scale 0 and zero codes.  Inputs must be finite.  ik_new must be NULL
+ * (PAGED_EUNSUPPORTED otherwise): indexer keys are not kept in e4m3 arenas.
  */
 int paged_kv_append(const void *k_new, const void *v_new, const void *ik_new, int32_t n_new,
                     const paged_kv *kv, void *ik, void *pooled, int32_t idx_dim, const paged_pg *pg,

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     make_pg,
     paged_attn_decode,
     paged_attn_decode_workspace,
+    paged_attn_decode_window,
+    paged_attn_decode_window_workspace,
     paged_attn_prefill,
     paged_attn_prefill_workspace,
     paged_block_scores_topk,

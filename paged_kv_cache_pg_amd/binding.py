@@ -52,6 +52,10 @@ _SIGS = {
     "paged_attn_decode": (c_int32, [c_void_p, c_int32, c_int32, POINTER(KvStruct), POINTER(PgStruct), c_void_p,
                                     c_int32, c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "paged_attn_decode_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
+    "paged_attn_decode_window": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(KvStruct),
+                                           POINTER(PgStruct), c_void_p, c_int32, c_int32, c_float, c_void_p,
+                                           c_void_p, c_size_t, c_void_p]),
+    "paged_attn_decode_window_workspace": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "paged_attn_prefill": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(KvStruct),
                                      POINTER(PgStruct), c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "paged_attn_prefill_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
@@ -157,6 +161,20 @@ def paged_attn_decode(q, q_dtype: int, n_q_heads: int, kv: KvStruct, pg: PgStruc
     _check(lib().paged_attn_decode(_p(q), q_dtype, n_q_heads, ctypes.byref(kv), ctypes.byref(pg), _p(seq_lens),
                                    n_streams, max_len, scale, _p(out), _p(workspace), wb, _stream(stream)),
            "paged_attn_decode")
+
+
+def paged_attn_decode_window_workspace(n_streams: int, n_q_heads: int, n_window: int, max_len: int) -> int:
+    return int(lib().paged_attn_decode_window_workspace(n_streams, n_q_heads, n_window, max_len))
+
+
+def paged_attn_decode_window(q, q_dtype: int, n_q_heads: int, n_window: int, kv: KvStruct, pg: PgStruct, seq_lens,
+                             n_streams: int, max_len: int, scale: float, out, workspace,
+                             workspace_bytes: Optional[int] = None, stream=None):
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None and workspace is not None else (workspace_bytes or 0)
+    _check(lib().paged_attn_decode_window(_p(q), q_dtype, n_q_heads, n_window, ctypes.byref(kv), ctypes.byref(pg),
+                                          _p(seq_lens), n_streams, max_len, scale, _p(out), _p(workspace), wb,
+                                          _stream(stream)),
+           "paged_attn_decode_window")
 
 
 def paged_attn_prefill_workspace(n_q: int, n_q_heads: int, kv_len: int) -> int:

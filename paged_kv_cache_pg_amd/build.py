@@ -28,7 +28,8 @@ FLAGS = [
 
 # Per-source extra flags.  prefill.hip: MFMA accumulators in VGPRs, so the softmax's rescale of
 # the output accumulators does not move them between AGPRs and VGPRs every tile.
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -13,6 +13,10 @@ namespace {
 
 constexpr int64_t MAX_POS = (int64_t)1 << 30;
 
+#ifndef PAGED_DECODE_MFMA_BF16
+#define PAGED_DECODE_MFMA_BF16 0  // one-query decode of bf16 rows on the MFMA kernel
+#endif
+
 inline bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline int esize(int32_t dt) { return dt == PAGED_FP8_E4M3 ? 1 : dt == PAGED_BF16 ? 2 : 4; }
 // types of q, indexer keys, pooled and copied rows
@@ -76,16 +80,20 @@ size_t dec_ws(int32_t n_streams, int32_t n_q_heads, int64_t max_keys) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PAGED_OK : PAGED_EHIP; }
 
-int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged_kv* kv, const paged_pg* pg,
-                  const int32_t* lens, const int32_t* ids, int32_t k, int32_t n_streams, int32_t max_len,
-                  float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (n_streams < 0 || max_len < 0 || max_len > MAX_POS) return PAGED_EINVAL;
+// Decode, sparse decode (ids != NULL) and the windowed decode (nq > 1 queries a stream).
+int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq, const paged_kv* kv,
+                  const paged_pg* pg, const int32_t* lens, const int32_t* ids, int32_t k, int32_t n_streams,
+                  int32_t max_len, float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_streams < 0 || max_len < 0 || max_len > MAX_POS || nq < 1) return PAGED_EINVAL;
   int r = check_kv(kv, pg);
   if (r) return r;
   r = check_pg(pg, kv->dtype, max_len, ids != nullptr);
   if (r) return r;
   r = group_ok(n_q_heads, kv->n_kv_heads);
   if (r) return r;
+  // windows: 1 .. 4 queries, window x group <= 16, on bf16 or e4m3 rows
+  if (nq > 1 && (nq > 4 || nq * (n_q_heads / kv->n_kv_heads) > 16 || kv->dtype == PAGED_F32))
+    return PAGED_EUNSUPPORTED;
   // q has the rows' type; e4m3 rows take bf16 queries
   const int32_t q_want = kv->dtype == PAGED_FP8_E4M3 ? PAGED_BF16 : kv->dtype;
   if (q_dtype != q_want) return dtype_ok(q_dtype) ? PAGED_EUNSUPPORTED : PAGED_EINVAL;
@@ -98,7 +106,7 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
     if (k < 1 || !al(ids, 4) || (int64_t)k * 4 > MAX_POS) return PAGED_EINVAL;
     max_keys = (int64_t)4 * k;
   }
-  const size_t need = dec_ws(n_streams, n_q_heads, max_keys);
+  const size_t need = dec_ws(n_streams, n_q_heads * nq, max_keys);
   if (ws_bytes < need || (need > 0 && (ws == nullptr || !al(ws, 16)))) return PAGED_EWORKSPACE;
 
   DecArgs a;
@@ -115,15 +123,22 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged
   a.max_len = max_len;
   a.hq = n_q_heads;
   a.hkv = kv->n_kv_heads;
+  a.nq = nq;
   a.zscale = (float)((double)scale * 1.4426950408889634);
   int ns = dec_splits_max((int)max_keys);
   a.ns_max = ns < 1 ? 1 : ns;
-  const size_t rows = (size_t)n_streams * n_q_heads * a.ns_max;
+  const size_t rows = (size_t)n_streams * n_q_heads * nq * a.ns_max;
   a.part_o = (float*)ws;
   a.part_ml = (float*)((char*)a.part_o + rows * HD * sizeof(float));
   a.out = out;
   const int elem = fp8 ? 2 : kv->dtype == PAGED_BF16 ? 1 : 0;
-  return hip_status(launch_decode(a, elem, n_q_heads / kv->n_kv_heads, n_streams, stream));
+  const int G = n_q_heads / kv->n_kv_heads;
+  // bf16 and e4m3 rows take the MFMA decode; float32 rows the vector-ALU one
+  // Windows and e4m3 rows take the MFMA decode (e4m3 decode is ALU-bound on the vector units); one
+  // query over bf16 rows the vector-ALU decode, which measures faster there; float32 rows always the latter.
+  if (nq > 1 || fp8 || (elem == 1 && PAGED_DECODE_MFMA_BF16))
+    return hip_status(launch_decode_mfma(a, elem, G, n_streams, stream));
+  return hip_status(launch_decode(a, elem, G, n_streams, stream));
 }
 
 int rows_common(int gather, void* lin, int64_t ss, int64_t sh, int64_t sp, void* region, int32_t n_heads,
@@ -168,8 +183,20 @@ size_t paged_attn_decode_workspace(int32_t n_streams, int32_t n_q_heads, int32_t
 int paged_attn_decode(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged_kv* kv, const paged_pg* pg,
                       const int32_t* seq_lens, int32_t n_streams, int32_t max_len, float scale, float* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, q_dtype, n_q_heads, kv, pg, seq_lens, nullptr, 0, n_streams, max_len, scale, out,
+  return decode_common(q, q_dtype, n_q_heads, 1, kv, pg, seq_lens, nullptr, 0, n_streams, max_len, scale, out,
                        workspace, workspace_bytes, stream);
+}
+
+size_t paged_attn_decode_window_workspace(int32_t n_streams, int32_t n_q_heads, int32_t n_window, int32_t max_len) {
+  if (n_window < 1) return 0;
+  return dec_ws(n_streams, n_q_heads * n_window, max_len);
+}
+
+int paged_attn_decode_window(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t n_window, const paged_kv* kv,
+                             const paged_pg* pg, const int32_t* seq_lens, int32_t n_streams, int32_t max_len,
+                             float scale, float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(q, q_dtype, n_q_heads, n_window, kv, pg, seq_lens, nullptr, 0, n_streams, max_len, scale,
+                       out, workspace, workspace_bytes, stream);
 }
 
 size_t paged_sparse_attn_workspace(int32_t n_streams, int32_t n_q_heads, int32_t k) {
@@ -182,7 +209,7 @@ int paged_sparse_attn(const void* q, int32_t q_dtype, int32_t n_q_heads, const p
                       int32_t max_len, float scale, float* out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   if (block_ids == nullptr || k < 1) return PAGED_EINVAL;
-  return decode_common(q, q_dtype, n_q_heads, kv, pg, n_selected, block_ids, k, n_streams, max_len, scale, out,
+  return decode_common(q, q_dtype, n_q_heads, 1, kv, pg, n_selected, block_ids, k, n_streams, max_len, scale, out,
                        workspace, workspace_bytes, stream);
 }
 

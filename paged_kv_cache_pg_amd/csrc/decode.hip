@@ -30,7 +30,7 @@
 // a score is zscale * k_scale * (q . codes) and a probability enters PV as
 // p * v_scale (the softmax sum keeps p).  The scales of a tile's keys are read
 // through the same page lookup as its rows and staged in LDS beside key_at.
-#include "internal.h"
+#include "split.h"
 
 namespace paged {
 
@@ -49,59 +49,17 @@ namespace {
 #ifndef PAGED_DEC_RING_FP8_SHORT
 #define PAGED_DEC_RING_FP8_SHORT 4
 #endif
-#ifndef PAGED_DEC_MAX_SPLITS
-#define PAGED_DEC_MAX_SPLITS 16  // splits a stream at most
-#endif
 #ifndef PAGED_DEC_WG_PER_CU
 #define PAGED_DEC_WG_PER_CU 1    // workgroups a CU the register budget is set for
 #endif
-#ifndef PAGED_DEC_NT
-#define PAGED_DEC_NT 1           // streamed K/V loads marked nontemporal
-#endif
-#ifndef PAGED_DEC_NWAVE
-#define PAGED_DEC_NWAVE 8        // waves a workgroup (a split is shared by its waves)
-#endif
-
-constexpr int TILE = 64;
-constexpr int NWAVE = PAGED_DEC_NWAVE;
-constexpr int WGS = 64 * NWAVE;
-
-constexpr int MAX_SPLITS = PAGED_DEC_MAX_SPLITS;
-
-__host__ __device__ inline int dec_tiles(int n) { return (n + TILE - 1) / TILE; }
-// Tiles a split: a multiple of the waves a workgroup, so that a stream never has more than MAX_SPLITS splits.
-__host__ __device__ inline int dec_tps(int ntiles) {
-  const int t = (ntiles + NWAVE * MAX_SPLITS - 1) / (NWAVE * MAX_SPLITS);
-  return NWAVE * (t < 1 ? 1 : t);
-}
-__host__ __device__ inline int dec_splits(int n) {
-  const int nt = dec_tiles(n);
-  if (nt == 0) return 0;
-  const int tps = dec_tps(nt);
-  return (nt + tps - 1) / tps;
-}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// Row types: float32, bf16, e4m3 codes (+ float32 scale a row).
-enum : int { ET_F32 = 0, ET_BF16 = 1, ET_FP8 = 2 };
 template <int ET> struct Rows {
   static constexpr int ROWB = ET == ET_F32 ? HD * 4 : ET == ET_BF16 ? HD * 2 : HD;  // K/V row bytes
   static constexpr int QROWB = ET == ET_F32 ? HD * 4 : HD * 2;                    // q row bytes
   static constexpr int NCQ = ROWB / 256;  // 16-byte K chunks a lane in QK (16 lanes a key)
   static constexpr int NQC = QROWB / 256; // 16-byte q chunks a lane and head
 };
-
-// 16-byte load of streamed K/V data (read once: no reuse to keep in cache).
-__device__ __forceinline__ uint4 ld_stream(const char* p) {
-#if PAGED_DEC_NT
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-#else
-  const u32x4_t v = *(const u32x4_t*)p;
-#endif
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ __forceinline__ uint2 ld_stream8(const char* p) {
 #if PAGED_DEC_NT
@@ -203,13 +161,6 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
-// Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Partial dot product of a lane's q chunks with its K chunks (16 lanes a key).
 //   f32:  4 chunks of 4 dims;  bf16: 2 chunks of 8 dims;  e4m3: one chunk of 16 codes against 16 bf16 q dims
 // (two q chunks), the codes widened to bf16 pairs exactly (every e4m3 value is a bf16 value).
@@ -264,13 +215,6 @@ __device__ __forceinline__ void pv_unpack(const uint4& v0, const uint4& v1, floa
     f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
     f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
   }
-}
-
-// Number of keys a stream attends to: its length (dense) or 4 x its selected blocks (sparse).
-__device__ __forceinline__ int stream_keys(const DecArgs& a, int s) {
-  const int v = a.lens[s];
-  if (a.ids != nullptr) return 4 * min(max(v, 0), a.ids_stride);
-  return min(max(v, 0), a.max_len);
 }
 
 // One 4-key step of loads, the same register footprint for both kinds: a K step (QK, 16 lanes a
@@ -575,11 +519,13 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 // Merge a (stream, head)'s split partials in split order; thread d owns dimension d.
 static_assert(MAX_SPLITS <= 64, "the combine kernel keeps one split a lane of its first wave");
 
+// A stream's output rows are its nq window queries x hq heads (one query in plain decode).
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   __shared__ float s_scale[MAX_SPLITS];
   __shared__ float s_L;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int64_t row0 = ((int64_t)s * a.hq + h) * a.ns_max;
+  const int64_t rows = (int64_t)a.hq * a.nq;
+  const int64_t row0 = ((int64_t)s * rows + h) * a.ns_max;
   // Every load is issued before any result is needed: the split count (from the stream's length),
   // the splits' (m, l) and this thread's output dimension of every split slot.  Slots past the
   // stream's split count hold stale values and are never used.
@@ -594,7 +540,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     lv = a.part_ml[(row0 + lc) * 2 + 1];
   }
   const int ns = dec_splits(n);
-  float* outp = a.out + ((int64_t)s * a.hq + h) * HD;
+  float* outp = a.out + ((int64_t)s * rows + h) * HD;
   if (ns == 0) {
     outp[d] = 0.f;
     return;
@@ -649,8 +595,7 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq, n_streams), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_decode_combine(a, n_streams, st);
 }
 
 template <int ET>
@@ -666,10 +611,16 @@ hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
 
 }  // namespace
 
+// Split slots a (stream, query, head) needs in the workspace.
 int dec_splits_max(int max_keys) {
   const int nt = dec_tiles(max_keys);
   const int a = (nt + NWAVE - 1) / NWAVE;
   return a < MAX_SPLITS ? a : MAX_SPLITS;
+}
+
+hipError_t launch_decode_combine(const DecArgs& a, int n_streams, hipStream_t st) {
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq * a.nq, n_streams), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecArgs& a, int elem, int G, int n_streams, hipStream_t st) {

@@ -24,16 +24,20 @@ struct DecArgs {
   int32_t max_len;        // bound on lengths and on block positions
   int32_t hq;
   int32_t hkv;
+  int32_t nq;             // queries a stream (1, or the window of the windowed decode)
   float zscale;           // softmax scale * log2(e)
-  int32_t ns_max;         // split slots a (stream, head) in the workspace
-  float* part_o;          // [S][Hq][ns_max][HD]
-  float* part_ml;         // [S][Hq][ns_max][2]
-  float* out;             // [S][Hq][HD]
+  int32_t ns_max;         // split slots a (stream, query, head) in the workspace
+  float* part_o;          // [S][nq][Hq][ns_max][HD]
+  float* part_ml;         // [S][nq][Hq][ns_max][2]
+  float* out;             // [S][nq][Hq][HD]
 };
 
 int dec_splits_max(int max_keys);
 // elem: 0 float32, 1 bf16, 2 e4m3 codes with a float32 scale a row (q bf16)
 hipError_t launch_decode(const DecArgs& a, int elem, int G, int n_streams, hipStream_t st);
+// The MFMA decode (bf16 or e4m3 rows, q bf16): nq window queries x G heads <= 16 rows a KV head.
+hipError_t launch_decode_mfma(const DecArgs& a, int elem, int G, int n_streams, hipStream_t st);
+hipError_t launch_decode_combine(const DecArgs& a, int n_streams, hipStream_t st);
 
 // ---- prefill (prefill.hip) ------------------------------------------------
 struct PreArgs {

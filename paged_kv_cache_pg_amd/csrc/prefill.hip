@@ -22,19 +22,13 @@
 // buffers tile t-1 left, and are waited for at its end.  Workgroups of one KV head are spread
 // round-robin so that consecutive workgroups (one per XCD) share KV heads two XCDs apiece.
 #include "internal.h"
+#include "mfma.h"
 
 namespace paged {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PF_ROWS = 128;        // (query, head) rows a workgroup
 constexpr int PF_WAVES = 4;         // 32 rows a wave
@@ -45,46 +39,6 @@ constexpr int CH = ROWB / 16;       // 16-byte chunks a row (32)
 constexpr int TILEB = PF_KT * ROWB; // bytes a K or V tile in LDS (rows unpadded, chunks swizzled)
 constexpr int LD_PER_WAVE = PF_KT * CH / PF_THREADS;  // 1 KB global->LDS loads a wave a tile (8)
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a row's running max may lag behind before O is rescaled
-
-__device__ __forceinline__ void swap32(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(r[0]);
-  y = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap16(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(r[0]);
-  y = __uint_as_float(r[1]);
-}
-// max / sum over the four lanes of a lane column (l, l^16, l^32, l^48); every lane gets the same bits.
-__device__ __forceinline__ float col_max(float x) {
-  float y = x;
-  swap32(x, y);
-  x = fmaxf(x, y);
-  y = x;
-  swap16(x, y);
-  return fmaxf(x, y);
-}
-__device__ __forceinline__ float col_sum(float x) {
-  float y = x;
-  swap32(x, y);
-  x = x + y;
-  y = x;
-  swap16(x, y);
-  return x + y;
-}
-
-__device__ __forceinline__ bf16x4 lds_tr16(const char* lds_base, int byte_off) {
-  const lds_s16x4* p = (const lds_s16x4*)((__attribute__((address_space(3))) const char*)lds_base + byte_off);
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-}
-
-// LDS tiles hold 64 rows of 512 bytes with the 16-byte chunks of a row permuted, so that the
-// fragment reads hit distinct banks: K chunk c of row r sits at slot c ^ (r mod 16) (the 16 rows
-// of a K fragment read), V chunk c at slot c ^ 2(r mod 8) (the 8 rows x 2 chunks of 32 lanes of a
-// transpose read).
-__device__ __forceinline__ int k_slot(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int v_slot(int row, int c) { return c ^ ((row & 7) << 1); }
 
 template <int G>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
@@ -168,14 +122,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   // j = (c16%4)/2 and x = r1 mod 8 = (4u + c16/4) mod 8, i.e. 2(db ^ x) + j, so with db = 8dh + dl
   // the offset is voff[dl] + 256 dh + 16384 s2 + 8192 h.
   int koff[8], voff[8];
-  {
-    const int x = (4 * u + (c16 >> 2)) & 7, j = (c16 & 3) >> 1, hb = (c16 & 1) * 8;
-    const int r0 = 4 * u + (c16 >> 2);
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) koff[ds] = c16 * ROWB + k_slot(c16, 4 * ds + u) * 16;
+  for (int ds = 0; ds < 8; ++ds) koff[ds] = c16 * ROWB + k_slot(c16, 4 * ds + u) * 16;
 #pragma unroll
-    for (int dl = 0; dl < 8; ++dl) voff[dl] = r0 * ROWB + (2 * (dl ^ x) + j) * 16 + hb;
-  }
+  for (int dl = 0; dl < 8; ++dl) voff[dl] = vt_offset(u, c16, dl);
 
   // S^T of one tile: sacc[kb][rb] holds keys 16kb + 4u + i of rows 16rb + c16, summed over ds
   // in order.  Steps run ds-major so that the 8 accumulators take turns (a dependent MFMA is

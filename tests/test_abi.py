@@ -177,3 +177,22 @@ def test_fp8_refusals():
     # indexer-key, pooled and copied rows are never e4m3
     assert L.paged_pool_blocks(FAKE, FAKE, 128, F8, ctypes.byref(pg8), FAKE, FAKE, 3, 131072, 0) == E
     assert L.paged_rows_store(FAKE, 0, 0, 256, FAKE, 4, 256, F8, ctypes.byref(pg8), FAKE, FAKE, 1, 160, 0) == E
+
+
+def test_window_refusals():
+    U = B.PAGED_EUNSUPPORTED
+    L = B.lib()
+
+    def win(W, hq=32, dtype=B.PAGED_BF16, ws=FAKE):
+        kv = B.make_kv(FAKE, FAKE, dtype, 4, 256)
+        pg = _pg()
+        wsb = P.paged_attn_decode_window_workspace(4, hq, W, 40960)
+        return L.paged_attn_decode_window(FAKE, 1, hq, W, ctypes.byref(kv), ctypes.byref(pg), FAKE, 4, 40960, 0.0625,
+                                          FAKE, ws, wsb, 0)
+    assert win(3) == U                   # 3 queries x 8 heads > 16 columns
+    assert win(5, hq=4) == U             # windows of at most 4
+    assert win(2, dtype=B.PAGED_F32) == U
+    assert win(0) == B.PAGED_EINVAL
+    assert win(2, ws=0) == B.PAGED_EWORKSPACE
+    # workspace rows scale with the window
+    assert P.paged_attn_decode_window_workspace(4, 32, 2, 40960) == 2 * P.paged_attn_decode_workspace(4, 32, 40960)

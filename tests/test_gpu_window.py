@@ -1,0 +1,108 @@
+"""GPU parity of the windowed decode (paged_attn_decode_window): W queries at the end of each
+stream's cache, query w seeing keys 0 .. L - W + w (the reading of PR #1169's fn_attn_chunks_ahead).
+
+Bar: within 2e-3 (max-norm relative per row) of the float64 oracle, paged == contiguous bit for
+bit, a window of one equal to paged_attn_decode bit for bit, short streams (L < W) give zero rows
+for the queries that see nothing.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import paged_kv_cache_pg_amd as P  # noqa: E402
+from paged_kv_cache_pg_amd.inputs import (  # noqa: E402
+    bf16_bits_to_f32, draw_e4m3_codes, draw_row_scales, f32_to_bf16_bits, make_table, make_workload)
+from gpu_util import Placed, PlacedFp8, decode, dev, guarded_out, out_guards_intact, rel_err_rows, TOL  # noqa: E402
+
+D = 256
+
+
+def _window(pl, q, hq, W, lens_t, S, max_len, dtype, out=None):
+    ws = torch.zeros(max(16, P.paged_attn_decode_window_workspace(S, hq, W, max_len)), dtype=torch.uint8,
+                     device="cuda")
+    if out is None:
+        out = torch.empty((S, W, hq, D), dtype=torch.float32, device="cuda")
+    P.paged_attn_decode_window(q, P.PAGED_BF16, hq, W, pl.kv, pl.pg, lens_t, S, max_len, 1 / 16, out, ws)
+    return out
+
+
+CASES = [
+    # lens, ptok, Hq, Hkv, W
+    ([1, 2, 63, 64, 65, 700], 16, 16, 2, 2),
+    ([4113, 3], 256, 8, 2, 4),
+    ([500, 129, 1], 48, 4, 2, 3),
+    ([1030], 128, 3, 3, 4),
+]
+
+
+@pytest.mark.parametrize("lens,ptok,hq,hkv,W", CASES)
+def test_window_bf16_matches_oracle_and_paged_equals_contiguous(lens, ptok, hq, hkv, W):
+    w = make_workload(90 + W, lens, ptok, hq, hkv, dtype="bf16", table_kind="shuffled")
+    rng = np.random.default_rng(190 + W)
+    q = f32_to_bf16_bits(rng.standard_normal((len(lens), W, hq, D), dtype=np.float32))
+    pl, pc = Placed(w, paged=True), Placed(w, paged=False)
+    qd = dev(q)
+    S, ml = len(lens), max(lens)
+    buf, out = guarded_out((S, W, hq, D))
+    _window(pl, qd, hq, W, pl.lens, S, ml, "bf16", out=out)
+    torch.cuda.synchronize()
+    assert out_guards_intact(buf)
+    got = out.cpu().numpy()
+    oc = _window(pc, qd, hq, W, pc.lens, S, ml, "bf16").cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oc.view(np.uint32)), "paged != contiguous"
+    ref = O.decode_window(bf16_bits_to_f32(q).astype(np.float64), w.as_f64("K"), w.as_f64("V"), lens, 1 / 16)
+    assert rel_err_rows(got, ref) <= TOL
+    for s, L in enumerate(lens):
+        for k in range(W):
+            if L - W + k < 0:
+                assert np.all(got[s, k] == 0), (s, k)
+
+
+def test_window_of_one_is_decode_bitwise():
+    lens = [3000, 77, 0, 1]
+    w = make_workload(95, lens, 64, 32, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w, paged=True)
+    qd = dev(w.q)
+    dec = decode(pl, qd, 1 / 16).cpu().numpy()
+    win = _window(pl, qd.view(4, 1, 32, D), 32, 1, pl.lens, 4, max(lens), "bf16").cpu().numpy()
+    assert np.array_equal(dec.view(np.uint32), win[:, 0].view(np.uint32))
+
+
+def test_window_fp8_matches_oracle_and_paged_equals_contiguous():
+    lens, hkv, hq, W, ptok = [1500, 5, 64], 2, 8, 4, 32
+    rng = np.random.default_rng(97)
+    S, cap = len(lens), max(lens)
+    KC, VC = draw_e4m3_codes(rng, (S, hkv, cap, D)), draw_e4m3_codes(rng, (S, hkv, cap, D))
+    KS, VS = draw_row_scales(rng, (S, hkv, cap)), draw_row_scales(rng, (S, hkv, cap))
+    q = f32_to_bf16_bits(rng.standard_normal((S, W, hq, D), dtype=np.float32))
+    table, n_pages = make_table("shuffled", [(l + ptok - 1) // ptok for l in lens], rng)
+    pl = PlacedFp8(lens, hkv, ptok, KC, VC, KS, VS, table=table, n_pages=n_pages)
+    pc = PlacedFp8(lens, hkv, ptok, KC, VC, KS, VS)
+    qd = dev(q)
+    got = _window(pl, qd, hq, W, pl.lens, S, cap, "fp8").cpu().numpy()
+    oc = _window(pc, qd, hq, W, pc.lens, S, cap, "fp8").cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oc.view(np.uint32))
+    ref = O.decode_window(bf16_bits_to_f32(q).astype(np.float64), O.e4m3_dequantize(KC, KS),
+                          O.e4m3_dequantize(VC, VS), lens, 1 / 16)
+    assert rel_err_rows(got, ref) <= TOL
+
+
+def test_window_full_size_sampled():
+    """4 streams x 40960 positions, 32 q / 4 KV heads, pages of 256 shuffled, a window of 2 (16 columns):
+    sampled rows against the oracle."""
+    S, L, HQ, HKV, W = 4, 40960, 32, 4, 2
+    w = make_workload(96, [L] * S, 256, HQ, HKV, dtype="bf16", table_kind="shuffled")
+    rng = np.random.default_rng(196)
+    q = f32_to_bf16_bits(rng.standard_normal((S, W, HQ, D), dtype=np.float32))
+    pl = Placed(w, paged=True)
+    got = _window(pl, dev(q), HQ, W, pl.lens, S, L, "bf16").cpu().numpy()
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    K, V = w.as_f64("K"), w.as_f64("V")
+    for s, k, h in ((0, 0, 0), (1, 1, 9), (3, 0, 31), (2, 1, 20)):
+        g = h // 8
+        ref = O.decode_window(qf[s:s + 1, :, h:h + 1], K[s:s + 1, g:g + 1], V[s:s + 1, g:g + 1], [L], 1 / 16)
+        assert rel_err_rows(got[s, k, h][None], ref[0, k, 0][None]) <= TOL, (s, k, h)
