@@ -32,6 +32,11 @@ namespace {
 #define PAGED_DECM_RING 8        // 16-byte loads in flight a lane
 #endif
 
+// A K fragment load takes 64 bytes of each of 16 rows; the other half of each 128-byte line is read
+// a few loads later, so K loads are ordinary cached loads (marked nontemporal, the lines left before
+// their second half was read and K was fetched from HBM twice).  V loads read whole lines: streamed.
+__device__ __forceinline__ uint4 ld_k(const char* p) { return *(const uint4*)p; }
+
 constexpr int HALF = 32;                 // keys a PV half tile
 constexpr int VROWB = 2 * HD;            // a staged V row (bf16) in LDS
 constexpr int VBUF = HALF * VROWB;       // V staging a wave (16 KiB); the wave's partial O after the loop
@@ -135,7 +140,8 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
     }
     const int64_t off = s_keyat[w][tt & 1][key];
     ok = ok_t && off >= 0;
-    x = ld_stream((ok ? base + off : dummy) + boff);
+    const char* p = (ok ? base + off : dummy) + boff;
+    x = i < NK ? ld_k(p) : ld_stream(p);
   };
 
   f32x4 oacc[16];
