@@ -32,17 +32,30 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_355_198
-DECODE_TRAFFIC_SOURCES = "40e3b6e65999d665"
+DECODE_TRAFFIC_BYTES = 676_362_901
+DECODE_TRAFFIC_SOURCES = "3d917b40c923700a"
+# The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
+FP8_TRAFFIC_BYTES = 346_399_278
+FP8_TRAFFIC_SOURCES = "511a7c48cfbc18dd"
+
+_DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
+                   "paged_kv_cache_pg_amd/csrc/common.h")
+_FP8_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode_mfma.hip", "paged_kv_cache_pg_amd/csrc/decode.hip",
+                "paged_kv_cache_pg_amd/csrc/split.h", "paged_kv_cache_pg_amd/csrc/mfma.h",
+                "paged_kv_cache_pg_amd/csrc/common.h")
 
 
-def _decode_sources_hash() -> str:
+def _sources_hash(files=_DECODE_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/common.h"):
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _decode_sources_hash() -> str:
+    return _sources_hash(_DECODE_SOURCES)
 
 
 def log(msg: str):
@@ -561,7 +574,8 @@ def run_decode_fp8(args):
     out = {"us_per_step": round(ms_step * 1e3, 2), "GB_per_s": round(gbs, 1), "alg_bytes_per_launch": dec.alg_bytes,
            "avg_launch_us": round(ms_call * 1e3, 2), "median_launch_us": round(ms_med * 1e3, 2),
            "hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4), "oracle_max_rel_err": err,
-           "tokens_per_s": round(dec.S / (ms_step * 1e-3), 1)}
+           "tokens_per_s": round(dec.S / (ms_step * 1e-3), 1),
+           "traffic": FP8_TRAFFIC_BYTES if _sources_hash(_FP8_SOURCES) == FP8_TRAFFIC_SOURCES else None}
     del dec
     return out
 
