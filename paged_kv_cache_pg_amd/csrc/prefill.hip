@@ -7,12 +7,16 @@
 // offsets are staged in LDS.
 //
 // A workgroup owns 128 (query, head) rows -- 128/G queries x the G query heads of one KV
-// head -- so every K/V tile is read once for all G heads.  Each of its 4 waves owns 32 rows.
-// Per 64-key tile:
+// head -- so every K/V tile is read once for all G heads.  Each of its 8 waves owns 16 rows, so
+// two waves share a SIMD and one's softmax runs while the other's MFMAs do (four waves of 32
+// rows need 420 registers a wave, one wave a SIMD, and each wave then waits on its own chain of
+// QK MFMAs -> softmax -> PV MFMAs).  Per 64-key tile:
 //   S^T = K Q^T   (MFMA 16x16x32 bf16: A = K rows from LDS, B = Q^T kept in registers).
 //                 A lane's accumulators hold 4 keys of one row, so a row's statistics live
 //                 in the 4 lanes {c, c+16, c+32, c+48} and never leave a lane column.
-//   softmax       fp32 online max/sum in the log2 domain; causal mask key <= query position.
+//   softmax       fp32 online max/sum in the log2 domain; causal mask key <= query position,
+//                 applied only on tiles that cross the diagonal (a tile every row sees whole
+//                 takes no mask and no -inf tests).
 //                 A row's reference max is moved (and O rescaled) only when a tile's max
 //                 passes it by more than 8, so most tiles skip the rescale.
 //   O^T += V^T P^T  (MFMA; A = V^T via LDS transpose reads, B = P^T straight from the S^T
@@ -30,8 +34,18 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef PAGED_PF_RB
+#define PAGED_PF_RB 1               // 16-row blocks a wave (1: eight waves of 16 rows; 2: four of 32)
+#endif
+#ifndef PAGED_PF_QK_AHEAD
+#define PAGED_PF_QK_AHEAD 4         // K fragment reads ahead of their MFMAs
+#endif
+#ifndef PAGED_PF_PV_AHEAD
+#define PAGED_PF_PV_AHEAD 4         // V^T fragment reads (pairs) ahead of their MFMAs
+#endif
+constexpr int RB = PAGED_PF_RB;
 constexpr int PF_ROWS = 128;        // (query, head) rows a workgroup
-constexpr int PF_WAVES = 4;         // 32 rows a wave
+constexpr int PF_WAVES = PF_ROWS / (16 * RB);
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_KT = 64;           // keys a tile
 constexpr int ROWB = HD * 2;        // bytes a bf16 key / value row
@@ -57,22 +71,22 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   const int kmax = a.causal ? a.q_pos0 + q_last + 1 : kv_len;
   const int nt = (kmax + PF_KT - 1) / PF_KT;
 
-  // rows of this lane: r = 32w + 16rb + c16 -> query qi = r / G, head h = r % G
-  int lim[2];
-  bool vrow[2];
+  // rows of this lane: r = 16 RB w + 16rb + c16 -> query qi = r / G, head h = r % G
+  int lim[RB];
+  bool vrow[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * w + 16 * rb + c16;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 16 * RB * w + 16 * rb + c16;
     const int qi = q_begin + r / G;
     vrow[rb] = qi < a.n_q;
     lim[rb] = a.causal ? min(a.q_pos0 + qi + 1, kv_len) : kv_len;  // keys < lim are seen
   }
 
   // Q^T fragments (B operand): lane holds Q[row 16rb + c16][32ds + 8u .. +7]
-  bf16x8 qf[2][8];
+  bf16x8 qf[RB][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * w + 16 * rb + c16;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 16 * RB * w + 16 * rb + c16;
     const int qi = q_begin + r / G, h = r % G;
     const char* qp = (const char*)a.q + (((int64_t)qi * a.hq + (int64_t)g * G + h) * HD) * 2;
 #pragma unroll
@@ -131,8 +145,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   // in order.  Steps run ds-major so that the 8 accumulators take turns (a dependent MFMA is
   // 8 issues behind its predecessor); the K fragment of step (ds, kb) is read QK_AHEAD steps
   // before its two MFMAs.
-  auto qk = [&](const char* kbuf, f32x4 (&sacc)[4][2]) {
-    constexpr int QK_AHEAD = 4;
+  auto qk = [&](const char* kbuf, f32x4 (&sacc)[4][RB]) {
+    constexpr int QK_AHEAD = PAGED_PF_QK_AHEAD;
     auto kfrag = [&](int st) {
       const int ds = st >> 2, kb = st & 3;
       return *(const bf16x8*)(kbuf + koff[ds] + 16 * ROWB * kb);
@@ -143,32 +157,37 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 32; ++st) {
       const bf16x8 kf = ring[st % QK_AHEAD];
       if (st + QK_AHEAD < 32) ring[st % QK_AHEAD] = kfrag(st + QK_AHEAD);
       const int ds = st >> 2, kb = st & 3;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
         sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sacc[kb][rb], 0, 0, 0);
     }
     // keep one fragment read a step: reads QK_AHEAD steps ahead, two MFMAs a step
     __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
 #pragma unroll
     for (int st = 0; st < 32 - QK_AHEAD; ++st) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QK_AHEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, RB * QK_AHEAD, 0);
   };
 
-  f32x4 oacc[16][2];
+  f32x4 oacc[16][RB];
 #pragma unroll
   for (int db = 0; db < 16; ++db)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) oacc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = NEG_INF;
+    l_run[rb] = 0.f;
+  }
 
   // ---- prologue: K(0), V(0) into LDS ----
   stage_keyat(0, key_page(0));
@@ -187,23 +206,36 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     stage_keyat(t + 2, page_next);
     page_next = key_page(t + 3);
 
-    f32x4 s_cur[4][2];
+    f32x4 s_cur[4][RB];
     qk(s_k[t & 1], s_cur);
 
-    bf16x8 phi[2][2], plo[2][2];  // [32-key step][rb]
-    float alpha_rb[2];
+    bf16x8 phi[2][RB], plo[2][RB];  // [32-key step][rb]
+    float alpha_rb[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      // A tile every row of the block sees whole (below the diagonal) takes no mask, and its
+      // scores are finite, so exp2 needs no -inf test: one multiply, max, subtract, exp2 and add a score.
+      const bool full = __all(k0 + PF_KT <= lim[rb]);
       float z[4][4];
       float mx = NEG_INF;
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * kb + 4 * u + i;
-          z[kb][i] = key < lim[rb] ? s_cur[kb][rb][i] * a.zscale : NEG_INF;
-          mx = fmaxf(mx, z[kb][i]);
-        }
+          for (int i = 0; i < 4; ++i) {
+            z[kb][i] = s_cur[kb][rb][i] * a.zscale;
+            mx = fmaxf(mx, z[kb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * kb + 4 * u + i;
+            z[kb][i] = key < lim[rb] ? s_cur[kb][rb][i] * a.zscale : NEG_INF;
+            mx = fmaxf(mx, z[kb][i]);
+          }
+      }
       mx = col_max(mx);
       // The reference max moves only when the tile's max passes it by more than RESCALE_SLACK
       // (so P <= 2^RESCALE_SLACK): most tiles leave O untouched.
@@ -213,13 +245,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
       alpha_rb[rb] = alpha;
       float rs = 0.f;
       float p[4][4];
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = (z[kb][i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(z[kb][i] - m_new);
-          rs += p[kb][i];
-        }
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = __builtin_amdgcn_exp2f(z[kb][i] - m_new);
+            rs += p[kb][i];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = (z[kb][i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(z[kb][i] - m_new);
+            rs += p[kb][i];
+          }
+      }
       rs = col_sum(rs);
       l_run[rb] = l_run[rb] * alpha + rs;
       m_run[rb] = m_new;
@@ -240,11 +282,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     }
 
     // rescale O only when some row of the wave moved its reference max (multiplying by 1 is exact)
-    if (__ballot(alpha_rb[0] != 1.f || alpha_rb[1] != 1.f) != 0) {
+    bool any_move = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) any_move = any_move || alpha_rb[rb] != 1.f;
+    if (__ballot(any_move) != 0) {
 #pragma unroll
       for (int db = 0; db < 16; ++db)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) oacc[db][rb] *= alpha_rb[rb];
+        for (int rb = 0; rb < RB; ++rb) oacc[db][rb] *= alpha_rb[rb];
     }
 
     // ---- O^T += V(t)^T P(t)^T ----
@@ -253,7 +298,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     // issues behind its hi MFMA (each accumulator still adds hi then lo, s2 = 0 then 1).
     // Fragments are read PV_AHEAD steps ahead.
     {
-      constexpr int PV_AHEAD = 2;
+      constexpr int PV_AHEAD = PAGED_PF_PV_AHEAD;
       const char* vbuf = s_v[t & 1];
       auto vfrag = [&](int s2, int db) {
         const int o = voff[db & 7] + 256 * (db >> 3) + 32 * ROWB * s2;
@@ -278,21 +323,21 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             oacc[db0 + e][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[e], phi[s2][rb], oacc[db0 + e][rb], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             oacc[db0 + e][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[e], plo[s2][rb], oacc[db0 + e][rb], 0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 4 * PV_AHEAD, 0);
 #pragma unroll
       for (int st = 0; st < 16 - PV_AHEAD; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8 * PV_AHEAD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB * PV_AHEAD, 0);
     }
 
     // ---- K(t+1) and V(t+1) have landed; every wave is done with K(t) and V(t) ----
@@ -302,9 +347,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
 
   // ---- normalise and write: lane holds O^T[16db + 4u + i][row 16rb + c16] ----
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     if (!vrow[rb]) continue;
-    const int r = 32 * w + 16 * rb + c16;
+    const int r = 16 * RB * w + 16 * rb + c16;
     const int qi = q_begin + r / G, h = r % G;
     float* op = a.out + ((int64_t)qi * a.hq + (int64_t)g * G + h) * HD;
     const float inv = 1.f / l_run[rb];
