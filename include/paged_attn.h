@@ -210,8 +210,10 @@ int paged_pool_blocks(const void *ik, void *pooled, int32_t idx_dim, int32_t are
  *              arena_dtype is the arena's K/V type, which gives page_elems its byte size
  *   out_scores optional device [n_streams][max_len/4] float64 (NULL: kept in workspace)
  *   workspace  >= paged_topk_workspace(n_streams, max_len, k) bytes, 16-byte aligned: per-stream
- *              coarse score histograms (4096 uint32) and, without out_scores, the scores;
- *              contents undefined after the call.  Calls sharing a workspace must not overlap.
+ *              coarse score histograms (4096 uint32), per 1024 blocks the selection counts,
+ *              taken bits and candidate (key, id) pairs (12 KiB + 136 bytes) and, without
+ *              out_scores, the scores; contents undefined after the call.  Calls sharing a
+ *              workspace must not overlap.
  * Scores are NaN-free for finite inputs; NaN scores are undefined behaviour.
  */
 int paged_block_scores_topk(const void *qi, int32_t qi_dtype, int32_t n_idx_heads, int32_t idx_dim,

@@ -310,8 +310,24 @@ int paged_block_scores_topk(const void* qi, int32_t qi_dtype, int32_t n_idx_head
   a.idx_dim = idx_dim;
   a.max_blocks = max_blocks;
   a.k = k;
-  a.hist = (uint32_t*)workspace;
-  a.scores = out_scores ? out_scores : (double*)((char*)workspace + (size_t)n_streams * 4096 * sizeof(uint32_t));
+  {
+    // workspace layout: see topk_workspace_bytes
+    const size_t S = (size_t)n_streams;
+    const int nsel = topk_nsel(max_blocks);
+    char* p = (char*)workspace;
+    a.hist = (uint32_t*)p;
+    p += S * 4096 * sizeof(uint32_t);
+    a.sel_cnt = (uint32_t*)p;
+    p += S * nsel * 2 * sizeof(uint32_t);
+    a.sel_bits = (uint32_t*)p;
+    p += S * nsel * 32 * sizeof(uint32_t);
+    a.sel_key = (uint64_t*)p;
+    p += S * nsel * 1024 * sizeof(uint64_t);
+    a.sel_id = (int32_t*)p;
+    p += S * nsel * 1024 * sizeof(int32_t);
+    a.nsel = nsel;
+    a.scores = out_scores ? out_scores : (double*)p;
+  }
   a.out_ids = out_ids;
   a.out_count = out_count;
   return hip_status(launch_scores_topk(a, qi_dtype == PAGED_BF16, n_streams, stream));

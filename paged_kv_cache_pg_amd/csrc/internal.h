@@ -79,10 +79,16 @@ struct TopkArgs {
   int32_t k;
   double* scores;         // [S][max_blocks]
   uint32_t* hist;         // workspace [S][4096]: coarse score histograms
+  uint32_t* sel_cnt;      // workspace [S][nsel][2]: a selection workgroup's taken and candidate counts
+  uint32_t* sel_bits;     // workspace [S][nsel * 32]: taken bits, a bit a block
+  uint64_t* sel_key;      // workspace [S][nsel][1024]: a selection workgroup's bin-T keys
+  int32_t* sel_id;        // workspace [S][nsel][1024]: and their ids
+  int32_t nsel;           // selection workgroups a stream: ceil(max_blocks / 1024)
   int32_t* out_ids;       // [S][k]
   int32_t* out_count;     // [S]
 };
 size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_external);
+int topk_nsel(int max_blocks);
 hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hipStream_t st);
 
 // ---- row stores / gathers and the addressing hook (rows.hip) ----------------

@@ -241,6 +241,9 @@ constexpr int TK_CMAX = 4096;       // candidates ranked in LDS
 constexpr int TK_AMAX = 8192;       // k at most for the list path
 constexpr int TK_BATCH = 16;        // score chunks a thread reads at once
 constexpr int HK_ITEMS = 1024;      // scores a histogram workgroup
+constexpr int SEL_ITEMS = 1024;     // blocks a selection workgroup
+constexpr int SEL_THREADS = 256;
+constexpr int TK_SBITS = 1 << 18;   // blocks a stream whose selected candidates are marked in LDS
 constexpr int HK_THREADS = 256;
 
 __device__ __forceinline__ uint64_t order_key(double x) {
@@ -337,6 +340,101 @@ __global__ __launch_bounds__(HK_THREADS) void hist_kernel(TopkArgs a) {
   }
 }
 
+// Step 2a: selection spread over the stream.  Workgroup b of stream s owns blocks [1024 b, 1024 b + 1024):
+// it finds bin T and krem from the histogram itself, then writes the taken bits of its blocks (bin > T),
+// its count of them, and its bin-T (key, id) pairs with their count.  No counter is shared between
+// workgroups; inside one, a wave adds its ballot counts with one LDS atomic.
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(TopkArgs a) {
+  __shared__ uint64_t s_tmp[SEL_THREADS / 64 + 1];
+  __shared__ uint32_t s_T, s_nt, s_nc;
+  const int s = blockIdx.y, b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = stream_blocks(a, s);
+  const int k = a.k;
+  const int i0 = b * SEL_ITEMS;
+  if (nb <= k || i0 >= nb) return;  // nothing to select, or past the stream's blocks
+  if (tid == 0) {
+    s_nt = 0;
+    s_nc = 0;
+  }
+  // the bin of the k-th block: thread t owns bins 4095 - 16t .. 4080 - 16t (descending)
+  {
+    constexpr int BPT = TK_BINS / SEL_THREADS;
+    const uint32_t* gh = a.hist + (int64_t)s * TK_BINS;
+    const int top = TK_BINS - 1 - BPT * tid;
+    uint32_t c[BPT];
+    uint64_t loc = 0;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      c[r] = gh[top - r];
+      loc += c[r];
+    }
+    // exclusive scan over the workgroup, in thread (= descending bin) order
+    uint64_t x = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    uint64_t before = x - loc;
+    for (int v = 0; v < w; ++v) before += s_tmp[v];
+    if (before < (uint64_t)k && before + loc >= (uint64_t)k) {
+#pragma unroll
+      for (int r = 0; r < BPT; ++r) {
+        if (before + c[r] >= (uint64_t)k) {
+          s_T = (uint32_t)(top - r);
+          break;
+        }
+        before += c[r];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t T = s_T;
+  const double* sc = a.scores + (int64_t)s * a.max_blocks;
+  double x[SEL_ITEMS / SEL_THREADS];
+#pragma unroll
+  for (int r = 0; r < SEL_ITEMS / SEL_THREADS; ++r) {
+    const int i = i0 + r * SEL_THREADS + tid;
+    x[r] = i < nb ? sc[i] : (double)NEG_INF;
+  }
+  uint64_t* keys = a.sel_key + ((int64_t)s * a.nsel + b) * SEL_ITEMS;
+  int32_t* cids = a.sel_id + ((int64_t)s * a.nsel + b) * SEL_ITEMS;
+  uint32_t* bits = a.sel_bits + (int64_t)s * a.nsel * (SEL_ITEMS / 32);
+#pragma unroll
+  for (int r = 0; r < SEL_ITEMS / SEL_THREADS; ++r) {
+    const int i = i0 + r * SEL_THREADS + tid;
+    const uint32_t cb = coarse_bin(x[r]);
+    const bool taken = i < nb && cb > T, cand = i < nb && cb == T;
+    const uint64_t tm = __ballot(taken), cm = __ballot(cand);
+    // the 64 blocks of this wave and round are 64 consecutive ids: two words of taken bits
+    if (lane == 0) {
+      const int word = (i - lane) >> 5;
+      bits[word] = (uint32_t)tm;
+      bits[word + 1] = (uint32_t)(tm >> 32);
+    }
+    uint32_t cbase = 0;
+    if (lane == 0) {
+      atomicAdd(&s_nt, (uint32_t)__popcll(tm));
+      if (cm) cbase = atomicAdd(&s_nc, (uint32_t)__popcll(cm));
+    }
+    cbase = __shfl(cbase, 0);
+    if (cand) {
+      const uint32_t slot = cbase + lanes_below(cm);
+      keys[slot] = order_key(x[r]);
+      cids[slot] = i;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* cnt = a.sel_cnt + ((int64_t)s * a.nsel + b) * 2;
+    cnt[0] = s_nt;
+    cnt[1] = s_nc;
+  }
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ int32_t s_aid[TK_AMAX];   // ids taken (unordered until the final ranking)
   __shared__ uint64_t s_ckey[TK_CMAX]; // candidates of bin T: exact keys and ids
@@ -348,6 +446,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t s_T, s_na, s_nc;
   __shared__ int s_krem, s_done;
   __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_sbit[TK_SBITS / 64];   // selected bin-T blocks, a bit a block
+  __shared__ uint32_t s_woff[TK_THREADS];      // per selection workgroup: candidate offsets, then output bases
+  __shared__ uint32_t s_wsel[TK_THREADS];      // per selection workgroup: selected candidates
 
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -413,6 +514,89 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   }
   const uint32_t T = s_T;
   int krem = s_krem;
+
+  // ---- fast path: the selection workgroups' taken bits and candidates ----
+  const int nw = (nb + SEL_ITEMS - 1) / SEL_ITEMS;  // selection workgroups of this stream
+  if (nw <= TK_THREADS && nb <= TK_SBITS) {
+    const uint32_t* cnt = a.sel_cnt + (int64_t)s * a.nsel * 2;
+    const uint32_t my_nt = tid < nw ? cnt[2 * tid] : 0u, my_nc = tid < nw ? cnt[2 * tid + 1] : 0u;
+    uint64_t nc64;
+    const uint32_t coff = (uint32_t)wg_scan64(my_nc, s_tmp, &nc64);
+    const int nc = (int)nc64;
+    if (nc <= TK_CMAX) {
+      s_woff[tid] = coff;
+      s_wsel[tid] = 0;
+      for (int q = tid; q < (nb + 63) / 64; q += TK_THREADS) s_sbit[q] = 0;
+      __syncthreads();
+      // gather the candidates: flat index f lives in workgroup b = the last with s_woff[b] <= f
+      for (int f = tid; f < nc; f += TK_THREADS) {
+        int lo = 0, hi = nw - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_woff[mid] <= (uint32_t)f) lo = mid;
+          else hi = mid - 1;
+        }
+        const int64_t src = ((int64_t)s * a.nsel + lo) * SEL_ITEMS + (f - (int)s_woff[lo]);
+        s_ckey[f] = a.sel_key[src];
+        s_cid[f] = a.sel_id[src];
+      }
+      __syncthreads();
+      // exact ranks, four lanes a candidate (each counts a quarter of the others); the krem ahead
+      // are selected and marked, the one of rank krem - 1 is the threshold
+      for (int c0 = 0; c0 < nc; c0 += TK_THREADS / 4) {
+        const int c = c0 + (tid >> 2), q = tid & 3;
+        int r = 0;
+        uint64_t kc = 0;
+        int32_t ic = 0;
+        if (c < nc) {
+          kc = s_ckey[c];
+          ic = s_cid[c];
+          const int o0 = (nc * q) >> 2, o1 = (nc * (q + 1)) >> 2;
+#pragma unroll 8
+          for (int o = o0; o < o1; ++o) {
+            const uint64_t ko = s_ckey[o];
+            const int32_t io = s_cid[o];
+            r += (int)((ko > kc) | ((ko == kc) & (io < ic)));
+          }
+        }
+        r += __shfl_xor(r, 1);
+        r += __shfl_xor(r, 2);
+        if (c < nc && q == 0 && r < krem) {
+          atomicOr((unsigned long long*)&s_sbit[ic >> 6], 1ull << (ic & 63));
+          atomicAdd(&s_wsel[ic / SEL_ITEMS], 1u);
+        }
+      }
+      __syncthreads();
+      // where each selection workgroup's ids start in the output: its taken blocks and its selected
+      // candidates, scanned in workgroup (= id) order
+      {
+        uint64_t tot;
+        const uint32_t base = (uint32_t)wg_scan64(tid < nw ? (uint64_t)my_nt + s_wsel[tid] : 0ull, s_tmp, &tot);
+        s_woff[tid] = base;
+      }
+      __syncthreads();
+      // the taken ids in id order: a wave takes selection workgroups w, w + 16, ...; lanes 0..15 load
+      // the 16 taken-bit words of its 16 chunks, then each chunk's ids go out with one ballot-free mask
+      const uint64_t* bits = (const uint64_t*)(a.sel_bits + (int64_t)s * a.nsel * (SEL_ITEMS / 32));
+      const int nchunk = (nb + 63) / 64;
+      for (int b = w; b < nw; b += TK_WAVES) {
+        const int ch0 = b * (SEL_ITEMS / 64);
+        const uint64_t tw = (lane < SEL_ITEMS / 64 && ch0 + lane < nchunk) ? bits[ch0 + lane] : 0ull;
+        uint32_t run = s_woff[b];
+#pragma unroll
+        for (int j = 0; j < SEL_ITEMS / 64; ++j) {
+          const int ch = ch0 + j;
+          const uint64_t m = __shfl(tw, j) | (ch < nchunk ? s_sbit[ch] : 0ull);
+          const uint32_t pos = run + lanes_below(m);
+          if (((m >> lane) & 1ull) && pos < (uint32_t)k) ids[pos] = ch * 64 + lane;
+          run += (uint32_t)__popcll(m);
+        }
+      }
+      if (tid == 0) a.out_count[s] = k;
+      return;
+    }
+    __syncthreads();
+  }
 
   // ---- one sweep: ids above bin T are taken; bin T's scores become candidates ----
   const bool lists_fit = k <= TK_AMAX;
@@ -621,10 +805,20 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
+int topk_nsel(int max_blocks) { return (max_blocks + SEL_ITEMS - 1) / SEL_ITEMS; }
+
+// Workspace: coarse histograms [S][4096] u32 | selection counts [S][nsel][2] u32 | taken bits
+// [S][nsel][32] u32 | candidate keys [S][nsel][1024] u64 | candidate ids [S][nsel][1024] i32 | scores
+// [S][max_blocks] f64 (when the caller keeps none).  Every part starts 8-byte aligned.
 size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_external) {
   (void)k;
-  size_t b = (size_t)n_streams * TK_BINS * sizeof(uint32_t);  // coarse histograms
-  if (!scores_external) b += (size_t)n_streams * (size_t)max_blocks * sizeof(double);
+  const size_t S = (size_t)n_streams, nsel = (size_t)topk_nsel(max_blocks);
+  size_t b = S * TK_BINS * sizeof(uint32_t);
+  b += S * nsel * 2 * sizeof(uint32_t);
+  b += S * nsel * (SEL_ITEMS / 32) * sizeof(uint32_t);
+  b += S * nsel * SEL_ITEMS * sizeof(uint64_t);
+  b += S * nsel * SEL_ITEMS * sizeof(int32_t);
+  if (!scores_external) b += S * (size_t)max_blocks * sizeof(double);
   return b;
 }
 
@@ -647,6 +841,11 @@ hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hi
   if (a.max_blocks > 0) {
     dim3 grid((a.max_blocks + HK_ITEMS - 1) / HK_ITEMS, n_streams);
     hipLaunchKernelGGL(hist_kernel, grid, dim3(HK_THREADS), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.max_blocks > 0) {
+    hipLaunchKernelGGL(select_kernel, dim3(a.nsel, n_streams), dim3(SEL_THREADS), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -100,7 +100,8 @@ def test_workspace_sizes():
     assert P.paged_attn_decode_workspace(1, 8, 300) == 1 * 8 * 1 * 258 * 4
     assert P.paged_attn_decode_workspace(0, 8, 300) == 0
     assert P.paged_sparse_attn_workspace(3, 32, 512) == 3 * 32 * 4 * 258 * 4
-    assert P.paged_topk_workspace(3, 131072, 512) == 3 * 4096 * 4 + 3 * 32768 * 8
+    # histograms, then per 1024 blocks: 2 counts, 32 words of taken bits, 1024 (u64 key, i32 id) pairs
+    assert P.paged_topk_workspace(3, 131072, 512) == 3 * 4096 * 4 + 3 * 32 * (8 + 128 + 1024 * 12) + 3 * 32768 * 8
 
 
 def test_sparse_pool_topk_refusals():

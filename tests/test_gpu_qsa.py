@@ -274,3 +274,24 @@ def test_topk_register_path_bound_with_a_wide_table():
     table = np.zeros((2, stride), np.int32)
     table[:, :w.table.shape[1]] = w.table
     _topk_checked(w, Placed(w, table=table), 512, max_len=131076)
+
+
+def test_topk_k_beyond_the_list_bound():
+    """k = 9000 of 40,000 blocks: the taken ids go straight from the selection bits to the output."""
+    w = make_workload(62, [160000, 30000], 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128,
+                      n_idx_heads=4)
+    _topk_checked(w, Placed(w), 9000)
+
+
+def test_topk_heavy_ties_take_the_radix_path():
+    """More bin-T candidates than the ranking holds: every score equal over 5,000 and 4,250 blocks
+    (the first k ids), then integer-valued keys over 10,000 blocks, both against the oracle."""
+    w = make_workload(63, [20000, 17000], 64, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128,
+                      n_idx_heads=4)
+    w.IK[:] = f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    _topk_checked(w, Placed(w), 700)
+    w = make_workload(64, [40000], 64, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=4)
+    rng = np.random.default_rng(8)
+    w.IK = f32_to_bf16_bits(rng.integers(-1, 2, size=w.IK.shape).astype(np.float32))
+    w.qI = f32_to_bf16_bits(rng.integers(-1, 2, size=w.qI.shape).astype(np.float32))
+    _topk_checked(w, Placed(w), 300)
