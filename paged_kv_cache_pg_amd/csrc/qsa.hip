@@ -436,7 +436,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(TopkArgs a) {
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ int32_t s_aid[TK_AMAX];   // ids taken (unordered until the final ranking)
+  __shared__ __attribute__((aligned(16))) int32_t s_aid[TK_AMAX];  // ids taken (unordered until the final ranking)
   __shared__ uint64_t s_ckey[TK_CMAX]; // candidates of bin T: exact keys and ids
   __shared__ int32_t s_cid[TK_CMAX];
   __shared__ uint32_t s_dig[256];
@@ -447,8 +447,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ int s_krem, s_done;
   __shared__ uint64_t s_prefix;
   __shared__ uint64_t s_sbit[TK_SBITS / 64];   // selected bin-T blocks, a bit a block
-  __shared__ uint32_t s_woff[TK_THREADS];      // per selection workgroup: candidate offsets, then output bases
-  __shared__ uint32_t s_wsel[TK_THREADS];      // per selection workgroup: selected candidates
+  __shared__ uint32_t s_coff[TK_SBITS / SEL_ITEMS + 1];  // per selection workgroup: first candidate
+  __shared__ uint32_t s_tbase[TK_SBITS / SEL_ITEMS];     // per selection workgroup: taken blocks before it
+  __shared__ uint32_t s_wsel[TK_SBITS / SEL_ITEMS];      // per selection workgroup: selected candidates
+  __shared__ uint32_t s_woff[TK_SBITS / SEL_ITEMS];      // per selection workgroup: first output place
+  __shared__ uint32_t s_h2[256];
+  __shared__ int32_t s_l2id[TK_CMAX];
+  __shared__ uint64_t s_kmin, s_kmax;
+  __shared__ uint32_t s_n2;
+  __shared__ int s_over;
 
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -480,6 +487,255 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         if (j8 + u < J) f(j8 + u, item_id(j8 + u), t[u]);
     }
   };
+
+  // ---- fast path: the selection workgroups' counts, taken bits and bin-T candidates ----
+  // Every load that depends on nothing computed here is issued first, so their latencies overlap.
+  const int nw = (nb + SEL_ITEMS - 1) / SEL_ITEMS;  // selection workgroups of this stream (<= 256)
+  if (nb <= TK_SBITS) {
+    const int nchunk = (nb + 63) / 64;
+    // candidates, speculatively: thread t holds slot t % P of selection workgroup t / P (slots past
+    // the workgroup's count are ignored)
+    const int P = TK_THREADS / nw;
+    const int cb = tid / P, cj = tid - cb * P;
+    uint64_t ck = 0;
+    int32_t ci = 0;
+    if (cb < nw) {
+      const int64_t src = ((int64_t)s * a.nsel + cb) * SEL_ITEMS + cj;
+      ck = a.sel_key[src];
+      ci = a.sel_id[src];
+    }
+    // taken bits: lane l of wave w holds chunk word l % 16 of selection workgroup w + 16 (l / 16)
+    const uint64_t* bits = (const uint64_t*)(a.sel_bits + (int64_t)s * a.nsel * (SEL_ITEMS / 32));
+    const int tch = (w + TK_WAVES * (lane >> 4)) * (SEL_ITEMS / 64) + (lane & 15);
+    const uint64_t tw = tch < nchunk ? bits[tch] : 0ull;
+    // counts: wave 0, lane l holds selection workgroups 4l .. 4l + 3 (taken, candidates)
+    if (w == 0) {
+      const uint32_t* cnt = a.sel_cnt + (int64_t)s * a.nsel * 2;
+      uint32_t nt[4], nc[4], st = 0, sc = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int b = 4 * lane + r;
+        const uint2 v = b < nw ? *(const uint2*)(cnt + 2 * b) : make_uint2(0u, 0u);
+        nt[r] = v.x;
+        nc[r] = v.y;
+        st += v.x;
+        sc += v.y;
+      }
+      uint32_t it = st, ic = sc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(it, off), z = __shfl_up(ic, off);
+        if (lane >= off) {
+          it += y;
+          ic += z;
+        }
+      }
+      uint32_t pt = it - st, pc = ic - sc;
+      bool over = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int b = 4 * lane + r;
+        if (b < nw) {
+          s_tbase[b] = pt;
+          s_coff[b] = pc;
+          s_wsel[b] = 0;
+          over |= nc[r] > (uint32_t)P;
+        }
+        pt += nt[r];
+        pc += nc[r];
+      }
+      over = __ballot(over) != 0;
+      if (lane == 63) {
+        s_coff[nw] = pc;  // = every candidate
+        s_na = pt;        // = every taken block
+        s_nc = pc;
+        s_over = over;
+        s_kmin = ~0ull;
+        s_kmax = 0;
+        s_n2 = 0;
+      }
+    } else if (w == 1) {
+      for (int q = lane; q < 256; q += 64) s_h2[q] = 0;
+    }
+    for (int q = tid; q < nchunk; q += TK_THREADS) s_sbit[q] = 0;
+    __syncthreads();
+    const int NC = (int)s_nc;
+    if (NC <= TK_CMAX) {
+      const int krem = k - (int)s_na;  // 1 <= krem <= NC: bin T holds the k-th block
+      // the candidates into one list (in selection workgroup order), with their smallest and largest key
+      uint64_t kmn = ~0ull, kmx = 0;
+      if (cb < nw) {
+        const uint32_t o = s_coff[cb];
+        if (cj < (int)(s_coff[cb + 1] - o)) {
+          s_ckey[o + cj] = ck;
+          s_cid[o + cj] = ci;
+          kmn = ck;
+          kmx = ck;
+        }
+      }
+      if (s_over) {  // a selection workgroup holds more than P candidates: the rest one by one
+        for (int f = tid; f < NC; f += TK_THREADS) {
+          int lo = 0, hi = nw - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_coff[mid] <= (uint32_t)f) lo = mid;
+            else hi = mid - 1;
+          }
+          const int j = f - (int)s_coff[lo];
+          if (j >= P) {
+            const int64_t src = ((int64_t)s * a.nsel + lo) * SEL_ITEMS + j;
+            const uint64_t key = a.sel_key[src];
+            s_ckey[f] = key;
+            s_cid[f] = a.sel_id[src];
+            kmn = key < kmn ? key : kmn;
+            kmx = key > kmx ? key : kmx;
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t y0 = __shfl_xor(kmn, off), y1 = __shfl_xor(kmx, off);
+        kmn = y0 < kmn ? y0 : kmn;
+        kmx = y1 > kmx ? y1 : kmx;
+      }
+      if (lane == 0 && kmx != 0) {
+        atomicMin((unsigned long long*)&s_kmin, (unsigned long long)kmn);
+        atomicMax((unsigned long long*)&s_kmax, (unsigned long long)kmx);
+      }
+      __syncthreads();
+      // a 256-bin histogram of the candidates' keys above the smallest one, at the resolution that
+      // spreads them over the bins; sub-bin T2 holds the krem-th
+      const uint64_t kmin = s_kmin, span = s_kmax - kmin;
+      const int shift = span < 256 ? 0 : 56 - __builtin_clzll(span);  // (span >> shift) <= 255
+      for (int f = tid; f < NC; f += TK_THREADS) lds_count(s_h2, (uint32_t)((s_ckey[f] - kmin) >> shift));
+      __syncthreads();
+      if (w == 0) {
+        // lane l owns sub-bins 255-4l .. 252-4l (descending)
+        uint32_t c4[4], loc = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          c4[r] = s_h2[255 - 4 * lane - r];
+          loc += c4[r];
+        }
+        uint32_t incl = loc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        uint32_t above = incl - loc;
+        if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (above + c4[r] >= (uint32_t)krem) {
+              s_T = (uint32_t)(255 - 4 * lane - r);
+              s_krem = krem - (int)above;
+              break;
+            }
+            above += c4[r];
+          }
+        }
+      }
+      __syncthreads();
+      // candidates above sub-bin T2 are selected; those in it are listed for an exact ranking
+      const uint32_t T2 = s_T;
+      const int k2 = s_krem;
+      uint64_t* s_k2 = (uint64_t*)s_aid;  // keys of the sub-bin T2 list (s_aid is free on this path)
+      auto select = [&](int32_t id) {
+        atomicOr((unsigned long long*)&s_sbit[id >> 6], 1ull << (id & 63));
+        atomicAdd(&s_wsel[id / SEL_ITEMS], 1u);
+      };
+      for (int f = tid; f < NC; f += TK_THREADS) {
+        const uint64_t key = s_ckey[f];
+        const uint32_t sub = (uint32_t)((key - kmin) >> shift);
+        if (sub > T2) {
+          select(s_cid[f]);
+        } else if (sub == T2) {
+          const uint32_t slot = atomicAdd(&s_n2, 1u);
+          s_k2[slot] = key;
+          s_l2id[slot] = s_cid[f];
+        }
+      }
+      __syncthreads();
+      // exact ranks inside sub-bin T2, four lanes a member (each counts a quarter of the others)
+      const int n2 = (int)s_n2;
+      for (int c0 = 0; c0 < n2; c0 += TK_THREADS / 4) {
+        const int c = c0 + (tid >> 2), q = tid & 3;
+        int r = 0;
+        uint64_t kc = 0;
+        int32_t ic = 0;
+        if (c < n2) {
+          kc = s_k2[c];
+          ic = s_l2id[c];
+          const int o0 = (n2 * q) >> 2, o1 = (n2 * (q + 1)) >> 2;
+          for (int o = o0; o < o1; ++o) {
+            const uint64_t ko = s_k2[o];
+            const int32_t io = s_l2id[o];
+            r += (int)((ko > kc) | ((ko == kc) & (io < ic)));
+          }
+        }
+        r += __shfl_xor(r, 1);
+        r += __shfl_xor(r, 2);
+        if (c < n2 && q == 0 && r < k2) select(ic);
+      }
+      __syncthreads();
+      // where each selection workgroup's ids start in the output: its taken blocks and its selected
+      // candidates, scanned in workgroup (= id) order by wave 0
+      if (w == 0) {
+        uint32_t v[4], loc = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int b = 4 * lane + r;
+          v[r] = b < nw ? s_wsel[b] : 0u;
+          loc += v[r];
+        }
+        uint32_t incl = loc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        uint32_t run = incl - loc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int b = 4 * lane + r;
+          if (b < nw) s_woff[b] = s_tbase[b] + run;
+          run += v[r];
+        }
+      }
+      __syncthreads();
+      // the ids in id order: a selection workgroup's 16 chunks in turn, each chunk's ids from its
+      // taken word (held since the start for the first 64 workgroups) or'ed with its selected word
+      auto emit = [&](int b, uint64_t word_of_lane, int lane0) {
+        uint32_t run = s_woff[b];
+#pragma unroll
+        for (int j = 0; j < SEL_ITEMS / 64; ++j) {
+          const int ch = b * (SEL_ITEMS / 64) + j;
+          const uint64_t m = __shfl(word_of_lane, lane0 + j) | (ch < nchunk ? s_sbit[ch] : 0ull);
+          const uint32_t pos = run + lanes_below(m);
+          if (((m >> lane) & 1ull) && pos < (uint32_t)k) ids[pos] = ch * 64 + lane;
+          run += (uint32_t)__popcll(m);
+        }
+      };
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = w + TK_WAVES * q;
+        if (b < nw) emit(b, tw, 16 * q);
+      }
+      for (int b = w + 4 * TK_WAVES; b < nw; b += TK_WAVES) {
+        const int ch = b * (SEL_ITEMS / 64) + lane;
+        const uint64_t t2 = (lane < SEL_ITEMS / 64 && ch < nchunk) ? bits[ch] : 0ull;
+        emit(b, t2, 0);
+      }
+      if (tid == 0) a.out_count[s] = k;
+      return;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      s_na = 0;
+      s_nc = 0;
+    }
+  }
 
   // ---- 2. the bin of the k-th block, from the coarse histogram ----
   if (tid == 0) {
@@ -514,89 +770,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   }
   const uint32_t T = s_T;
   int krem = s_krem;
-
-  // ---- fast path: the selection workgroups' taken bits and candidates ----
-  const int nw = (nb + SEL_ITEMS - 1) / SEL_ITEMS;  // selection workgroups of this stream
-  if (nw <= TK_THREADS && nb <= TK_SBITS) {
-    const uint32_t* cnt = a.sel_cnt + (int64_t)s * a.nsel * 2;
-    const uint32_t my_nt = tid < nw ? cnt[2 * tid] : 0u, my_nc = tid < nw ? cnt[2 * tid + 1] : 0u;
-    uint64_t nc64;
-    const uint32_t coff = (uint32_t)wg_scan64(my_nc, s_tmp, &nc64);
-    const int nc = (int)nc64;
-    if (nc <= TK_CMAX) {
-      s_woff[tid] = coff;
-      s_wsel[tid] = 0;
-      for (int q = tid; q < (nb + 63) / 64; q += TK_THREADS) s_sbit[q] = 0;
-      __syncthreads();
-      // gather the candidates: flat index f lives in workgroup b = the last with s_woff[b] <= f
-      for (int f = tid; f < nc; f += TK_THREADS) {
-        int lo = 0, hi = nw - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_woff[mid] <= (uint32_t)f) lo = mid;
-          else hi = mid - 1;
-        }
-        const int64_t src = ((int64_t)s * a.nsel + lo) * SEL_ITEMS + (f - (int)s_woff[lo]);
-        s_ckey[f] = a.sel_key[src];
-        s_cid[f] = a.sel_id[src];
-      }
-      __syncthreads();
-      // exact ranks, four lanes a candidate (each counts a quarter of the others); the krem ahead
-      // are selected and marked, the one of rank krem - 1 is the threshold
-      for (int c0 = 0; c0 < nc; c0 += TK_THREADS / 4) {
-        const int c = c0 + (tid >> 2), q = tid & 3;
-        int r = 0;
-        uint64_t kc = 0;
-        int32_t ic = 0;
-        if (c < nc) {
-          kc = s_ckey[c];
-          ic = s_cid[c];
-          const int o0 = (nc * q) >> 2, o1 = (nc * (q + 1)) >> 2;
-#pragma unroll 8
-          for (int o = o0; o < o1; ++o) {
-            const uint64_t ko = s_ckey[o];
-            const int32_t io = s_cid[o];
-            r += (int)((ko > kc) | ((ko == kc) & (io < ic)));
-          }
-        }
-        r += __shfl_xor(r, 1);
-        r += __shfl_xor(r, 2);
-        if (c < nc && q == 0 && r < krem) {
-          atomicOr((unsigned long long*)&s_sbit[ic >> 6], 1ull << (ic & 63));
-          atomicAdd(&s_wsel[ic / SEL_ITEMS], 1u);
-        }
-      }
-      __syncthreads();
-      // where each selection workgroup's ids start in the output: its taken blocks and its selected
-      // candidates, scanned in workgroup (= id) order
-      {
-        uint64_t tot;
-        const uint32_t base = (uint32_t)wg_scan64(tid < nw ? (uint64_t)my_nt + s_wsel[tid] : 0ull, s_tmp, &tot);
-        s_woff[tid] = base;
-      }
-      __syncthreads();
-      // the taken ids in id order: a wave takes selection workgroups w, w + 16, ...; lanes 0..15 load
-      // the 16 taken-bit words of its 16 chunks, then each chunk's ids go out with one ballot-free mask
-      const uint64_t* bits = (const uint64_t*)(a.sel_bits + (int64_t)s * a.nsel * (SEL_ITEMS / 32));
-      const int nchunk = (nb + 63) / 64;
-      for (int b = w; b < nw; b += TK_WAVES) {
-        const int ch0 = b * (SEL_ITEMS / 64);
-        const uint64_t tw = (lane < SEL_ITEMS / 64 && ch0 + lane < nchunk) ? bits[ch0 + lane] : 0ull;
-        uint32_t run = s_woff[b];
-#pragma unroll
-        for (int j = 0; j < SEL_ITEMS / 64; ++j) {
-          const int ch = ch0 + j;
-          const uint64_t m = __shfl(tw, j) | (ch < nchunk ? s_sbit[ch] : 0ull);
-          const uint32_t pos = run + lanes_below(m);
-          if (((m >> lane) & 1ull) && pos < (uint32_t)k) ids[pos] = ch * 64 + lane;
-          run += (uint32_t)__popcll(m);
-        }
-      }
-      if (tid == 0) a.out_count[s] = k;
-      return;
-    }
-    __syncthreads();
-  }
 
   // ---- one sweep: ids above bin T are taken; bin T's scores become candidates ----
   const bool lists_fit = k <= TK_AMAX;

@@ -295,3 +295,26 @@ def test_topk_heavy_ties_take_the_radix_path():
     w.IK = f32_to_bf16_bits(rng.integers(-1, 2, size=w.IK.shape).astype(np.float32))
     w.qI = f32_to_bf16_bits(rng.integers(-1, 2, size=w.qI.shape).astype(np.float32))
     _topk_checked(w, Placed(w), 300)
+
+
+def test_topk_many_candidates_in_few_selection_workgroups():
+    """Scores set block by block (indexer key = the block's value in dim 0, query = e0): 2,000 and
+    1,500 blocks tied in 16 values inside one coarse bin, packed into two selection workgroups, so
+    that they overflow the finishing workgroup's first gather and fill its sub-bins with ties."""
+    lens = [32768, 30001]
+    w = make_workload(65, lens, 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=4)
+    rng = np.random.default_rng(9)
+    v = np.zeros((2, 8192), np.float32)
+    v[:] = rng.uniform(-1.0, 0.9, size=v.shape)
+    v[0, :2000] = 1 + (np.arange(2000) % 16) / 128
+    v[0, 2000:3000] = 2.0
+    v[1, 6000:7500] = 1 + (np.arange(1500) * 7 % 16) / 128
+    v[1, :500] = 2.0
+    IK = np.zeros(w.IK.shape, np.float32)
+    IK[:, :, 0] = np.repeat(v, 4, axis=1)[:, :IK.shape[1]]
+    w.IK = f32_to_bf16_bits(IK)
+    qI = np.zeros(w.qI.shape, np.float32)
+    qI[:, 0, 0] = 1.0
+    w.qI = f32_to_bf16_bits(qI)
+    _topk_checked(w, Placed(w), 1500)
+    _topk_checked(w, Placed(w), 1000)
