@@ -537,6 +537,43 @@ def run_window(dec, args, W: int = 2):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tokens_per_s": round(dec.S * W / (ms * 1e-3), 1)}
 
 
+def run_rows(dec, args):
+    """Page-run save and restore of the decode workload's cache: every K and V row of the 4 streams
+    gathered from the paged arena into the contiguous layout [S][Hkv][L][D], then stored through the
+    table into a zeroed arena, which must come out equal to the first byte for byte."""
+    import torch
+    P = dec.P
+    S, H, L, D = dec.S, dec.HKV, dec.L, dec.D
+    lay = dec.lay
+    cont = torch.empty((2, S, H, L, D), dtype=torch.int16, device="cuda")
+    begin = torch.zeros(S, dtype=torch.int32, device="cuda")
+    src = dec.arenas[0]
+    dst = torch.zeros_like(src)
+    regions = ((0, lay.k_off), (1, lay.v_off))
+
+    def save(i):
+        for j, off in regions:
+            P.paged_rows_gather(cont[j], H * L * D, L * D, D, src.data_ptr() + off, H, D, P.PAGED_BF16, dec.pg,
+                                begin, dec.lens, S, L)
+
+    def restore(i):
+        for j, off in regions:
+            P.paged_rows_store(cont[j], H * L * D, L * D, D, dst.data_ptr() + off, H, D, P.PAGED_BF16, dec.pg,
+                               begin, dec.lens, S, L)
+    out = {}
+    moved = 2 * cont.numel() * 2  # bytes read + bytes written
+    for name, fn in (("save_gather", save), ("restore_store", restore)):
+        ms, _ = time_steps(fn, max(1, args.steps // 4), max(1, args.warmup // 4))
+        out[name] = {"us": round(ms * 1e3, 1), "bytes_moved": moved, "GB_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"rows {name}: {ms * 1e3:.1f} us, {moved / (ms * 1e-3) / 1e9:.0f} GB/s")
+    torch.cuda.synchronize()
+    out["restored_equals_original"] = bool(torch.equal(dst, src))
+    del cont, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_decode(args):
     dec = DecodeBench()
     ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
@@ -557,6 +594,7 @@ def run_decode(args):
                      "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
         "decode_window": run_window(dec, args),
+        "page_runs": run_rows(dec, args),
     }
     del dec
     return out
