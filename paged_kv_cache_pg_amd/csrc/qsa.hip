@@ -98,6 +98,39 @@ __device__ __forceinline__ void widen_q(const TopkArgs& a, int s, double* s_q) {
   }
 }
 
+// 128-dim rows: n_idx_heads x 128 query values (at most 2048), 16 bytes a lane at a time, every
+// load issued before the first is used.
+template <bool QBF16>
+__device__ __forceinline__ void widen_q128(const TopkArgs& a, int s, double* s_q) {
+  constexpr int PER = QBF16 ? 8 : 4;  // values a 16-byte chunk
+  const int m = a.n_idx_heads * 128;
+  const int nch = m / PER;
+  const uint4* src = (const uint4*)((const char*)a.qi + (int64_t)s * m * (QBF16 ? 2 : 4));
+  uint4 v[2048 / 4 / SC_NB];
+#pragma unroll
+  for (int j = 0; j < 2048 / 4 / SC_NB; ++j) {
+    const int c = threadIdx.x + j * SC_NB;
+    if (c < nch) v[j] = src[c];
+  }
+#pragma unroll
+  for (int j = 0; j < 2048 / 4 / SC_NB; ++j) {
+    const int c = threadIdx.x + j * SC_NB;
+    if (c < nch) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      double* d = s_q + c * PER;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (QBF16) {
+          d[2 * e] = (double)__uint_as_float(w[e] << 16);
+          d[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
+        } else {
+          d[e] = (double)__uint_as_float(w[e]);
+        }
+      }
+    }
+  }
+}
+
 template <bool QBF16>
 __global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) char s_stage[32 * SC_ROWB];
@@ -105,13 +138,16 @@ __global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
   __shared__ int64_t s_base[SC_NB];
   const int s = blockIdx.y, lane = threadIdx.x;
   if (blockIdx.x == 0) zero_hist(a, s);
-  const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+  // The table entries (every block below max_blocks has one) and the queries are read before the
+  // stream's length is known, so the three loads take one round trip; a lane's row base is used
+  // only for rows below the length.
   const int b0 = blockIdx.x * SC_NB;
-  if (b0 >= nb) return;
-  widen_q<QBF16>(a, s, s_q);
   const int b = b0 + lane;
+  s_base[lane] = pool_at(a.pg, s, min(b, a.max_blocks - 1), 128 * 4);
+  widen_q128<QBF16>(a, s, s_q);
+  const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+  if (b0 >= nb) return;
   const int nrows = min(SC_NB, nb - b0);
-  s_base[lane] = pool_at(a.pg, s, b < nb ? b : b0, 128 * 4);
   __syncthreads();
 
   // Rows move in two rounds of 32 (rows 0-31, then 32-63): lane (r1, ch) loads 16-byte chunk ch

@@ -318,3 +318,31 @@ def test_topk_many_candidates_in_few_selection_workgroups():
     w.qI = f32_to_bf16_bits(qI)
     _topk_checked(w, Placed(w), 1500)
     _topk_checked(w, Placed(w), 1000)
+
+
+@pytest.mark.parametrize("di,hi", [(128, 4), (128, 16), (64, 3)])
+def test_scores_topk_float32_rows_and_queries(di, hi):
+    """Float32 indexer keys and queries (the 128-wide kernel widens 16-byte query chunks; other
+    widths take the staged kernel), pooled, scored and selected bit for bit against the oracle."""
+    lens = [6000, 1001]
+    w = make_workload(66, lens, 64, 2, 1, dtype="f32", table_kind="shuffled", idx_dim=di, n_idx_heads=hi)
+    pl = Placed(w)
+    S, ml, k = len(lens), max(lens), 200
+    b0 = dev(np.zeros(S, np.int32))
+    b1 = dev(np.array([L // 4 for L in lens], np.int32))
+    P.paged_pool_blocks(pl.ik, pl.pooled, di, P.PAGED_F32, pl.pg, b0, b1, S, ml)
+    ids = torch.full((S, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(S, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, ml // 4), dtype=torch.float64, device="cuda")
+    ws = torch.empty(P.paged_topk_workspace(S, ml, k), dtype=torch.uint8, device="cuda")
+    P.paged_block_scores_topk(dev(w.qI), P.PAGED_F32, hi, di, pl.pooled, P.PAGED_F32, pl.pg, pl.lens, S, ml, k,
+                              ids, cnt, sc, ws)
+    torch.cuda.synchronize()
+    ids, cnt, sc = ids.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
+    pooled = O.pool(w.as_f64("IK"), lens)
+    for s, L in enumerate(lens):
+        want_sc = O.scores(w.as_f64("qI")[s], pooled[s])
+        assert np.array_equal(sc[s, :L // 4].view(np.uint64), want_sc.view(np.uint64)), s
+        want = O.topk(want_sc, k)
+        assert cnt[s] == len(want)
+        assert np.array_equal(ids[s, :len(want)], want), s
