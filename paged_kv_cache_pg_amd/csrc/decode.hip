@@ -147,17 +147,19 @@ struct QkReduce {
   }
 };
 
+// Over the 8 lanes l ^ {G, 2G, 4G} (the 8 partial sums of one head; with G < 8 each group of 8G lanes
+// holds a full copy).
 template <int G>
-__device__ __forceinline__ float head_max(float v) {
+__device__ __forceinline__ float head_max8(float v) {
 #pragma unroll
-  for (int off = G; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  for (int off = G; off < 8 * G; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
 
 template <int G>
-__device__ __forceinline__ float head_sum(float v) {
+__device__ __forceinline__ float head_sum8(float v) {
 #pragma unroll
-  for (int off = G; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  for (int off = G; off < 8 * G; off <<= 1) v += __shfl_xor(v, off);
   return v;
 }
 
@@ -254,7 +256,10 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   __shared__ float s_ks[FP8 ? NWAVE : 1][2][TILE];
   __shared__ float s_vs[FP8 ? NWAVE : 1][2][TILE];
 
+  // g: the group of G q heads g*G .. g*G+G-1; gk: their KV head (a KV head's q heads may be spread
+  // over 2^kvshift groups)
   const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  const int gk = g >> a.kvshift;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = stream_keys(a, s);
   const int nt = dec_tiles(n);
@@ -339,13 +344,13 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 
   // e4m3: the scales of a key, read through its page (the lookup its row takes); a masked key reads the
   // region's first scale and gets V scale 0.
-  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, g, pos, 4) : 0; };
+  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, gk, pos, 4) : 0; };
 
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
       const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
-      s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, g, pos0, ROWB) : (int64_t)-1;
+      s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
       if constexpr (FP8) {
         const int64_t so = scale_off(page0, pos0);
         const float ks = *(const float*)(a.ksb + so), vs = *(const float*)(a.vsb + so);
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
         if (i == 4) {
-          s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, g, pos1, ROWB) : (int64_t)-1;
+          s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
           if constexpr (FP8) {
             const int64_t so = scale_off(page1, pos1);
             ks1 = *(const float*)(a.ksb + so);
@@ -386,27 +391,31 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
           }
         }
         if (i == NSTEP) {
-          // Online softmax over tile t: lane handles flat entries k*64 + lane (head lane % G).
+          // Online softmax over tile t.  Lane l takes head hh = l % G and the 8 keys 8k + m (k = 0..7,
+          // in order) of m = (l / G) % 8; a head's 8 partial sums meet in a 3-level butterfly.  The
+          // tree is the same for every G (with G < 8 the lanes past 8G repeat the first 8G), so a
+          // head's bytes do not depend on how many heads share the wave.
           wave_lds_sync();
           float* sc = s_sc[w];
-          float ev[G];
+          const int hh = lane % G, m8 = (lane / G) & 7;
+          float ev[8];
           float tmax = NEG_INF;
 #pragma unroll
-          for (int k = 0; k < G; ++k) {
-            ev[k] = sc[k * 64 + lane];
+          for (int k = 0; k < 8; ++k) {
+            ev[k] = sc[(8 * k + m8) * G + hh];
             tmax = fmaxf(tmax, ev[k]);
           }
-          tmax = head_max<G>(tmax);
+          tmax = head_max8<G>(tmax);
           const float m_new = fmaxf(m_run, tmax);
           float tsum = 0.f;
 #pragma unroll
-          for (int k = 0; k < G; ++k) {
+          for (int k = 0; k < 8; ++k) {
             const float p = (ev[k] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[k] - m_new);
-            // the PV weight of key (k*64 + lane) / G carries its V scale; the running sum does not
-            sc[k * 64 + lane] = FP8 ? p * s_vs[w][t & 1][(k * 64 + lane) / G] : p;
+            // the PV weight of key 8k + m8 carries its V scale; the running sum does not
+            if (lane < 8 * G) sc[(8 * k + m8) * G + hh] = FP8 ? p * s_vs[w][t & 1][8 * k + m8] : p;
             tsum += p;
           }
-          tsum = head_sum<G>(tsum);
+          tsum = head_sum8<G>(tsum);
           const float alpha = (m_run == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
           l_run = l_run * alpha + tsum;
           m_run = m_new;
@@ -577,7 +586,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 // the arithmetic, so results do not depend on it.
 template <int ET, int G>
 hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
-  dim3 grid(a.ns_max, a.hkv, n_streams);
+  dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
   const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
   const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
   if constexpr (ET == ET_BF16) {
@@ -598,9 +607,23 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   return launch_decode_combine(a, n_streams, st);
 }
 
+// Short key lists (at most two tiles a wave) leave most of the GPU idle and each wave waiting on its
+// own loads: there a KV head's q heads are spread over up to 2^PAGED_DEC_HSPLIT workgroups, which read
+// the same K/V rows (the second read mostly from L2), so twice the waves keep loads in flight, each
+// with fewer registers.
+#ifndef PAGED_DEC_HSPLIT
+#define PAGED_DEC_HSPLIT 2
+#endif
 template <int ET>
-hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
-  switch (G) {
+hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
+  DecArgs a = a0;
+  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
+  const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
+  a.kvshift = 0;
+  if (short_keys) {
+    while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1) ++a.kvshift;
+  }
+  switch (G >> a.kvshift) {
     case 1: return launch_t<ET, 1>(a, n_streams, st);
     case 2: return launch_t<ET, 2>(a, n_streams, st);
     case 4: return launch_t<ET, 4>(a, n_streams, st);

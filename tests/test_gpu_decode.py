@@ -241,3 +241,35 @@ def test_tables_from_the_page_pool_after_churn():
     pl, pc, q, out = _run_case(w, 1 / 16)
     err = rel_err_rows(out, _oracle(w, 1 / 16))
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 4), (16, 4), (8, 4), (4, 4)])
+def test_bytes_independent_of_max_len(hq, hkv):
+    """Short key lists spread a KV head's q heads over several workgroups; a head's arithmetic is the
+    same either way, so a stream gives the same bytes with max_len = its own length (short path)
+    and with max_len = 20000 (long path, one workgroup a KV head), and the sparse call over all of
+    its blocks (k = 1024, short) equals the dense call with max_len = 20000 bit for bit."""
+    lens = [4096, 777]
+    w = make_workload(41, lens, 256, hq, hkv, dtype="bf16", table_kind="shuffled")
+    big = 20000
+    table = np.zeros((2, (big + 255) // 256), np.int32)
+    table[:, :w.table.shape[1]] = w.table
+    pl = Placed(w, table=table)
+    q = dev(w.q)
+    o_short = decode(pl, q, 1 / 16, max_len=max(lens)).cpu().numpy()
+    o_long = decode(pl, q, 1 / 16, max_len=big).cpu().numpy()
+    assert np.array_equal(o_short.view(np.uint32), o_long.view(np.uint32))
+    assert rel_err_rows(o_short, _oracle(w, 1 / 16)) <= TOL
+    k = 1024
+    ids = np.full((2, k), -1, np.int32)
+    cnt = np.zeros(2, np.int32)
+    for s, L in enumerate(lens):
+        ids[s, :L // 4] = np.arange(L // 4)
+        cnt[s] = L // 4
+    ws = torch.zeros(P.paged_sparse_attn_workspace(2, hq, k), dtype=torch.uint8, device="cuda")
+    sp = torch.empty((2, hq, 256), dtype=torch.float32, device="cuda")
+    P.paged_sparse_attn(q, P.PAGED_BF16, hq, pl.kv, pl.pg, dev(ids), dev(cnt), k, 2, big, 1 / 16, sp, ws)
+    torch.cuda.synchronize()
+    sp = sp.cpu().numpy()
+    # stream 1 (777 positions) has a ragged last block the block list cannot name: compare stream 0
+    assert np.array_equal(sp[0].view(np.uint32), o_long[0].view(np.uint32))
