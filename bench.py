@@ -361,6 +361,25 @@ class DecodeFp8Bench:
         self.P.paged_attn_decode(self.q, self.P.PAGED_BF16, self.HQ, self.kvs[i & 1], self.pg, self.lens, self.S,
                                  self.L, 1 / 16, self.out, self.ws)
 
+    def rows_of(self, arena, s: int, g: int):
+        """The stored codes and scales of stream s, KV head g, read back through the table (host)."""
+        import oracle as O
+        np = self.np
+        lay = O.PageLayout(self.HKV, self.D, self.PTOK, "fp8")
+        kc = np.empty((self.L, self.D), np.uint8)
+        vc = np.empty_like(kc)
+        ks = np.empty(self.L, np.float32)
+        vs = np.empty_like(ks)
+        for lp in range(self.L // self.PTOK):
+            p0 = lp * self.PTOK
+            o = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, self.D)
+            so = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, 4)
+            kc[p0:p0 + self.PTOK] = arena[lay.k_off + o:lay.k_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
+            vc[p0:p0 + self.PTOK] = arena[lay.v_off + o:lay.v_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
+            ks[p0:p0 + self.PTOK] = arena[lay.ks_off + so:lay.ks_off + so + self.PTOK * 4].view(np.float32)
+            vs[p0:p0 + self.PTOK] = arena[lay.vs_off + so:lay.vs_off + so + self.PTOK * 4].view(np.float32)
+        return kc, vc, ks, vs
+
     def check(self):
         """Sampled rows against the oracle over the stored codes x scales (outside the timed region)."""
         import oracle as O
@@ -370,26 +389,50 @@ class DecodeFp8Bench:
         out = self.out.cpu().numpy()
         arena = self.arenas[0].cpu().numpy()
         q = self.q.float().cpu().numpy().astype(np.float64)
-        lay = O.PageLayout(self.HKV, self.D, self.PTOK, "fp8")
         worst = 0.0
         for s, h in [(0, 0), (3, 31)]:
-            g = h // (self.HQ // self.HKV)
-            kc = np.empty((self.L, self.D), np.uint8)
-            vc = np.empty_like(kc)
-            ks = np.empty(self.L, np.float32)
-            vs = np.empty_like(ks)
-            for lp in range(self.L // self.PTOK):
-                p0 = lp * self.PTOK
-                o = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, self.D)
-                so = O.row_offset(self.table_np, self.PTOK, lay.page_elems, s, g, p0, 4)
-                kc[p0:p0 + self.PTOK] = arena[lay.k_off + o:lay.k_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
-                vc[p0:p0 + self.PTOK] = arena[lay.v_off + o:lay.v_off + o + self.PTOK * self.D].reshape(self.PTOK, -1)
-                ks[p0:p0 + self.PTOK] = arena[lay.ks_off + so:lay.ks_off + so + self.PTOK * 4].view(np.float32)
-                vs[p0:p0 + self.PTOK] = arena[lay.vs_off + so:lay.vs_off + so + self.PTOK * 4].view(np.float32)
+            kc, vc, ks, vs = self.rows_of(arena, s, h // (self.HQ // self.HKV))
             ref = O.decode(q[s:s + 1, h:h + 1], O.e4m3_dequantize(kc, ks)[None, None],
                            O.e4m3_dequantize(vc, vs)[None, None], [self.L], 1 / 16)[0, 0]
             worst = max(worst, float(np.max(np.abs(out[s, h] - ref)) / np.max(np.abs(ref))))
         return worst
+
+
+def run_sparse_fp8(dec, args, k: int = 512):
+    """Sparse attention over the e4m3 decode workload: k blocks of 4 rows a stream (ascending ids drawn
+    from a seeded generator), codes and scales read through the table; sampled rows against the oracle."""
+    import oracle as O
+    import numpy as np
+    import torch
+    P = dec.P
+    rng = np.random.default_rng(11)
+    ids = np.stack([np.sort(rng.choice(dec.L // 4, k, replace=False)) for _ in range(dec.S)]).astype(np.int32)
+    ids_d = torch.from_numpy(ids).cuda()
+    cnt = torch.full((dec.S,), k, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(P.paged_sparse_attn_workspace(dec.S, dec.HQ, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dec.out)
+
+    def step(i):
+        P.paged_sparse_attn(dec.q, P.PAGED_BF16, dec.HQ, dec.kvs[i & 1], dec.pg, ids_d, cnt, k, dec.S, dec.L, 1 / 16,
+                            out, ws)
+    ms, _ = time_steps(step, args.steps, args.warmup)
+    nbytes = (dec.S * dec.HKV * 4 * k * (dec.D + 4) * 2 + dec.q.numel() * 2 + ids.size * 4 + dec.S * 4
+              + out.numel() * 4)
+    step(0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    arena = dec.arenas[0].cpu().numpy()
+    q = dec.q.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for s, h in [(1, 5), (2, 30)]:
+        kc, vc, ks, vs = dec.rows_of(arena, s, h // (dec.HQ // dec.HKV))
+        pos = (4 * ids[s][:, None] + np.arange(4)[None, :]).reshape(-1)
+        ref = O.decode(q[s:s + 1, h:h + 1], O.e4m3_dequantize(kc[pos], ks[pos])[None, None],
+                       O.e4m3_dequantize(vc[pos], vs[pos])[None, None], [len(pos)], 1 / 16)[0, 0]
+        worst = max(worst, float(np.max(np.abs(got[s, h] - ref)) / np.max(np.abs(ref))))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"sparse e4m3 (k = {k}): {ms * 1e3:.1f} us, {gbs:.0f} GB/s; sampled rows within {worst:.2e} of the oracle")
+    return {"k": k, "us": round(ms * 1e3, 2), "alg_bytes": nbytes, "GB_per_s": round(gbs, 1), "oracle_max_rel_err": worst}
 
 
 class AppendBench:
@@ -613,7 +656,8 @@ def run_decode_fp8(args):
            "avg_launch_us": round(ms_call * 1e3, 2), "median_launch_us": round(ms_med * 1e3, 2),
            "hbm_frac": round(call_gbs / HBM_PEAK_GBS, 4), "oracle_max_rel_err": err,
            "tokens_per_s": round(dec.S / (ms_step * 1e-3), 1),
-           "traffic": FP8_TRAFFIC_BYTES if _sources_hash(_FP8_SOURCES) == FP8_TRAFFIC_SOURCES else None}
+           "traffic": FP8_TRAFFIC_BYTES if _sources_hash(_FP8_SOURCES) == FP8_TRAFFIC_SOURCES else None,
+           "sparse_attn_e4m3": run_sparse_fp8(dec, args)}
     del dec
     return out
 

@@ -71,7 +71,10 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
   __shared__ float s_m[NWAVE][16];
   __shared__ float s_l[NWAVE][16];
 
+  // g: the group of G q heads g*G .. g*G+G-1; gk: their KV head (a KV head's q heads may be spread
+  // over 2^kvshift groups; each q row is its own MFMA column, so the split changes no arithmetic)
   const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  const int gk = g >> a.kvshift;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, u = l >> 4, c16 = l & 15;
   const int n = stream_keys(a, s);
   const int nt = dec_tiles(n);
@@ -151,13 +154,13 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
   // e4m3: the scales of a key, read through its page (the lookup its row takes); a masked key reads the
   // region's first scale and gets V scale 0.
-  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, g, pos, 4) : 0; };
+  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, gk, pos, 4) : 0; };
 
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
       const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
-      s_keyat[w][0][l] = pos0 >= 0 ? pg_offset(a.pg, page0, g, pos0, ROWB) : (int64_t)-1;
+      s_keyat[w][0][l] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
       if constexpr (FP8) {
         const int64_t so = scale_off(page0, pos0);
         const float ks = *(const float*)(a.ksb + so), vs = *(const float*)(a.vsb + so);
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
       static_for<NS>([&](auto I) {
         constexpr int i = decltype(I)::value;
         if constexpr (i == 4) {
-          s_keyat[w][(t + 1) & 1][l] = pos1 >= 0 ? pg_offset(a.pg, page1, g, pos1, ROWB) : (int64_t)-1;
+          s_keyat[w][(t + 1) & 1][l] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
           if constexpr (FP8) {
             const int64_t so = scale_off(page1, pos1);
             ks1 = *(const float*)(a.ksb + so);
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
 template <int ET, int G, int W>
 hipError_t launch_w(const DecArgs& a, int n_streams, hipStream_t st) {
-  dim3 grid(a.ns_max, a.hkv, n_streams);
+  dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
   hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING>), grid, dim3(WGS), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -380,9 +383,20 @@ hipError_t launch_g(const DecArgs& a, int n_streams, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Short key lists (at most two tiles a wave): a KV head's q heads spread over up to
+// 2^PAGED_DECM_HSPLIT workgroups, as in the vector-ALU decode (more waves with loads in flight).
+#ifndef PAGED_DECM_HSPLIT
+#define PAGED_DECM_HSPLIT 2
+#endif
 template <int ET>
-hipError_t launch_e(const DecArgs& a, int G, int n_streams, hipStream_t st) {
-  switch (G) {
+hipError_t launch_e(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
+  DecArgs a = a0;
+  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
+  a.kvshift = 0;
+  if (dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE) {
+    while (a.kvshift < PAGED_DECM_HSPLIT && (G >> a.kvshift) > 1) ++a.kvshift;
+  }
+  switch (G >> a.kvshift) {
     case 1: return launch_g<ET, 1>(a, n_streams, st);
     case 2: return launch_g<ET, 2>(a, n_streams, st);
     case 4: return launch_g<ET, 4>(a, n_streams, st);
