@@ -280,6 +280,7 @@ constexpr int HK_ITEMS = 1024;      // scores a histogram workgroup
 constexpr int SEL_ITEMS = 1024;     // blocks a selection workgroup
 constexpr int SEL_THREADS = 256;
 constexpr int TK_SBITS = 1 << 18;   // blocks a stream whose selected candidates are marked in LDS
+constexpr int TK_CPT = TK_SBITS / 64 / 1024;  // 64-block chunks a thread at most in the id output (4)
 constexpr int HK_THREADS = 256;
 
 __device__ __forceinline__ uint64_t order_key(double x) {
@@ -484,9 +485,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ uint64_t s_prefix;
   __shared__ uint64_t s_sbit[TK_SBITS / 64];   // selected bin-T blocks, a bit a block
   __shared__ uint32_t s_coff[TK_SBITS / SEL_ITEMS + 1];  // per selection workgroup: first candidate
-  __shared__ uint32_t s_tbase[TK_SBITS / SEL_ITEMS];     // per selection workgroup: taken blocks before it
-  __shared__ uint32_t s_wsel[TK_SBITS / SEL_ITEMS];      // per selection workgroup: selected candidates
-  __shared__ uint32_t s_woff[TK_SBITS / SEL_ITEMS];      // per selection workgroup: first output place
   __shared__ uint32_t s_h2[256];
   __shared__ int32_t s_l2id[TK_CMAX];
   __shared__ uint64_t s_kmin, s_kmax;
@@ -540,10 +538,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
       ck = a.sel_key[src];
       ci = a.sel_id[src];
     }
-    // taken bits: lane l of wave w holds chunk word l % 16 of selection workgroup w + 16 (l / 16)
+    // taken bits: thread t holds the words of chunks (64 blocks) t*CPT .. t*CPT + CPT-1, in id order
     const uint64_t* bits = (const uint64_t*)(a.sel_bits + (int64_t)s * a.nsel * (SEL_ITEMS / 32));
-    const int tch = (w + TK_WAVES * (lane >> 4)) * (SEL_ITEMS / 64) + (lane & 15);
-    const uint64_t tw = tch < nchunk ? bits[tch] : 0ull;
+    const int cpt = (nchunk + TK_THREADS - 1) / TK_THREADS;  // <= TK_CPT
+    uint64_t tw[TK_CPT];
+#pragma unroll
+    for (int j = 0; j < TK_CPT; ++j) {
+      const int ch = tid * cpt + j;
+      tw[j] = (j < cpt && ch < nchunk) ? bits[ch] : 0ull;
+    }
     // counts: wave 0, lane l holds selection workgroups 4l .. 4l + 3 (taken, candidates)
     if (w == 0) {
       const uint32_t* cnt = a.sel_cnt + (int64_t)s * a.nsel * 2;
@@ -572,9 +575,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int b = 4 * lane + r;
         if (b < nw) {
-          s_tbase[b] = pt;
           s_coff[b] = pc;
-          s_wsel[b] = 0;
           over |= nc[r] > (uint32_t)P;
         }
         pt += nt[r];
@@ -677,10 +678,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
       const uint32_t T2 = s_T;
       const int k2 = s_krem;
       uint64_t* s_k2 = (uint64_t*)s_aid;  // keys of the sub-bin T2 list (s_aid is free on this path)
-      auto select = [&](int32_t id) {
-        atomicOr((unsigned long long*)&s_sbit[id >> 6], 1ull << (id & 63));
-        atomicAdd(&s_wsel[id / SEL_ITEMS], 1u);
-      };
+      auto select = [&](int32_t id) { atomicOr((unsigned long long*)&s_sbit[id >> 6], 1ull << (id & 63)); };
       for (int f = tid; f < NC; f += TK_THREADS) {
         const uint64_t key = s_ckey[f];
         const uint32_t sub = (uint32_t)((key - kmin) >> shift);
@@ -715,53 +713,28 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         if (c < n2 && q == 0 && r < k2) select(ic);
       }
       __syncthreads();
-      // where each selection workgroup's ids start in the output: its taken blocks and its selected
-      // candidates, scanned in workgroup (= id) order by wave 0
-      if (w == 0) {
-        uint32_t v[4], loc = 0;
+      // the ids in id order: thread t's chunks (taken word or'ed with selected word), their counts
+      // scanned over the workgroup in thread (= id) order, then each thread writes its chunks' ids
+      uint64_t mk[TK_CPT];
+      uint64_t mine = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int b = 4 * lane + r;
-          v[r] = b < nw ? s_wsel[b] : 0u;
-          loc += v[r];
-        }
-        uint32_t incl = loc;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
-        uint32_t run = incl - loc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int b = 4 * lane + r;
-          if (b < nw) s_woff[b] = s_tbase[b] + run;
-          run += v[r];
-        }
+      for (int j = 0; j < TK_CPT; ++j) {
+        const int ch = tid * cpt + j;
+        mk[j] = (j < cpt && ch < nchunk) ? (tw[j] | s_sbit[ch]) : 0ull;
+        mine += (uint64_t)__popcll(mk[j]);
       }
-      __syncthreads();
-      // the ids in id order: a selection workgroup's 16 chunks in turn, each chunk's ids from its
-      // taken word (held since the start for the first 64 workgroups) or'ed with its selected word
-      auto emit = [&](int b, uint64_t word_of_lane, int lane0) {
-        uint32_t run = s_woff[b];
+      uint64_t total;
+      uint32_t pos = (uint32_t)wg_scan64(mine, s_tmp, &total);
 #pragma unroll
-        for (int j = 0; j < SEL_ITEMS / 64; ++j) {
-          const int ch = b * (SEL_ITEMS / 64) + j;
-          const uint64_t m = __shfl(word_of_lane, lane0 + j) | (ch < nchunk ? s_sbit[ch] : 0ull);
-          const uint32_t pos = run + lanes_below(m);
-          if (((m >> lane) & 1ull) && pos < (uint32_t)k) ids[pos] = ch * 64 + lane;
-          run += (uint32_t)__popcll(m);
+      for (int j = 0; j < TK_CPT; ++j) {
+        uint64_t m = mk[j];
+        const int id0 = (tid * cpt + j) * 64;
+        while (m != 0) {
+          const int bit = __builtin_ctzll(m);
+          if (pos < (uint32_t)k) ids[pos] = id0 + bit;
+          ++pos;
+          m &= m - 1;
         }
-      };
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = w + TK_WAVES * q;
-        if (b < nw) emit(b, tw, 16 * q);
-      }
-      for (int b = w + 4 * TK_WAVES; b < nw; b += TK_WAVES) {
-        const int ch = b * (SEL_ITEMS / 64) + lane;
-        const uint64_t t2 = (lane < SEL_ITEMS / 64 && ch < nchunk) ? bits[ch] : 0ull;
-        emit(b, t2, 0);
       }
       if (tid == 0) a.out_count[s] = k;
       return;
