@@ -346,3 +346,10 @@ def test_scores_topk_float32_rows_and_queries(di, hi):
         want = O.topk(want_sc, k)
         assert cnt[s] == len(want)
         assert np.array_equal(ids[s, :len(want)], want), s
+
+
+def test_topk_stream_past_the_selection_bitmap():
+    """262,145 blocks in one stream (1,048,580 positions), one more than the finishing workgroup's
+    bitmap holds: the single-workgroup list path selects, bit for bit against the oracle."""
+    w = make_workload(67, [1048580], 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=1)
+    _topk_checked(w, Placed(w), 512)
