@@ -258,8 +258,12 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 
   // g: the group of G q heads g*G .. g*G+G-1; gk: their KV head (a KV head's q heads may be spread
   // over 2^kvshift groups)
-  const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
-  const int gk = g >> a.kvshift;
+  // blockIdx.y = j * Hkv + gk: the 2^kvshift workgroups of a KV head are Hkv * ns_max ids apart, so
+  // with the round-robin placement of workgroups on XCDs (linear id mod 8) they share one XCD's L2
+  // whenever Hkv * ns_max is a multiple of 8
+  const int s = blockIdx.z, c = blockIdx.x;
+  const int gk = (int)blockIdx.y % a.hkv;
+  const int g = (gk << a.kvshift) | ((int)blockIdx.y / a.hkv);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = stream_keys(a, s);
   const int nt = dec_tiles(n);

@@ -73,8 +73,12 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
   // g: the group of G q heads g*G .. g*G+G-1; gk: their KV head (a KV head's q heads may be spread
   // over 2^kvshift groups; each q row is its own MFMA column, so the split changes no arithmetic)
-  const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
-  const int gk = g >> a.kvshift;
+  // blockIdx.y = j * Hkv + gk: the 2^kvshift workgroups of a KV head are Hkv * ns_max ids apart, so
+  // with the round-robin placement of workgroups on XCDs (linear id mod 8) they share one XCD's L2
+  // whenever Hkv * ns_max is a multiple of 8
+  const int s = blockIdx.z, c = blockIdx.x;
+  const int gk = (int)blockIdx.y % a.hkv;
+  const int g = (gk << a.kvshift) | ((int)blockIdx.y / a.hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, u = l >> 4, c16 = l & 15;
   const int n = stream_keys(a, s);
   const int nt = dec_tiles(n);
