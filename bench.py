@@ -32,11 +32,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_367_116
-DECODE_TRAFFIC_SOURCES = "21b85e48ce3e6e28"
+DECODE_TRAFFIC_BYTES = 676_357_492
+DECODE_TRAFFIC_SOURCES = "a7848aa08d370ba9"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 346_368_415
-FP8_TRAFFIC_SOURCES = "3e23dd419decaa22"
+FP8_TRAFFIC_BYTES = 346_334_423
+FP8_TRAFFIC_SOURCES = "175b3b95cbc3e098"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")
