@@ -250,25 +250,34 @@ __global__ __launch_bounds__(SC_NB) void scores_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k, three steps (the block order a score sorts by: score descending, then
-// id ascending; -0.0 == +0.0):
-//  1. Coarse histogram (hist_kernel, many workgroups a stream): 4096 bins of the
-//     top 12 bits of the float32 order key of each score (sign, exponent, 3
+// Top-k (the block order a score sorts by: score descending, then id ascending;
+// -0.0 == +0.0), after the scores kernel:
+//  1. Coarse histogram (hist_kernel, a workgroup per 1024 scores): 4096 bins of
+//     the top 12 bits of the float32 order key of each score (sign, exponent, 3
 //     mantissa bits).  Rounding to float32 is monotone, so every score in a
 //     higher bin is larger than every score in a lower one.  The scores kernel
 //     zeroes the histogram; this kernel adds each workgroup's LDS histogram to it.
-//  2. Selection (topk_kernel, one workgroup a stream): the bin T where the count
-//     from the top reaches k holds the k-th block; krem blocks are still needed
-//     from it.  One sweep over the scores appends the ids of higher bins to an
-//     LDS list and bin T's (key, id) pairs to a candidate list; each candidate is
-//     ranked exactly (candidates ahead of it in the sort order, counted a wave at
-//     a time) and the krem of rank < krem join the list.
-//  3. Order: each listed id's place is the number of listed ids below it.
-// With more than TK_CMAX candidates (heavy ties) or k > TK_AMAX, a radix
-// refinement on the exact 64-bit keys of bin T finds the threshold instead (ties
-// at it go to the lowest ids), and a count sweep, a 16-entry scan of the waves'
-// counts and a write sweep compact the ids in order (wave w holds ids
-// [64 J w, 64 J (w+1))).
+//     Bin T, where the count from the top reaches k, holds the k-th block.
+//  2. Selection (select_kernel, a workgroup per 1024 blocks): each workgroup
+//     finds T from the histogram itself and writes, for its blocks, a taken bit
+//     per block (bin above T), its taken count, and its bin-T candidates (exact
+//     64-bit key, id) with their count.
+//  3. Finish (topk_kernel, a workgroup per stream): krem = k minus the taken
+//     count; the candidates are gathered into LDS, a 256-bin histogram of their
+//     keys above the smallest finds the sub-bin holding the krem-th, candidates
+//     above it are selected and the sub-bin's members ranked exactly (members
+//     ahead of each in the sort order); selected candidates are marked in an LDS
+//     bitmap.  The ids come out in id order: a thread per 64-block chunk or's
+//     the chunk's taken and selected words, and a scan of the chunks' counts
+//     gives each chunk's first output place.
+// Streams of more than TK_SBITS blocks take the single-workgroup list path: one
+// sweep lists the ids above bin T and bin T's candidates in LDS, each candidate
+// is ranked exactly, and each listed id's place is the number of listed ids below
+// it.  With more than TK_CMAX candidates (heavy ties) or, on the list path,
+// k > TK_AMAX, a radix refinement on the exact 64-bit keys of bin T finds the
+// threshold instead (ties at it go to the lowest ids), and a count sweep, a
+// 16-entry scan of the waves' counts and a write sweep compact the ids in order
+// (wave w holds ids [64 J w, 64 J (w+1))).
 // ---------------------------------------------------------------------------
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
