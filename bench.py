@@ -617,9 +617,59 @@ def run_rows(dec, args):
     return out
 
 
+def _sclk_now():
+    """Current shader clock levels (MHz) of the GPUs sysfs lists (the level marked '*'), or []."""
+    import glob
+    import re
+    out = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                for line in fh:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*mhz", line, re.I)
+                        if m:
+                            out.append(int(m.group(1)))
+        except OSError:
+            pass
+    return out
+
+
+class ClockSampler:
+    """Samples the highest current shader clock sysfs reports every 20 ms on a background thread."""
+
+    def __init__(self):
+        import threading
+        self.samples, self._stop = [], threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.wait(0.02):
+            c = _sclk_now()
+            if c:
+                self.samples.append(max(c))
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        import statistics
+        if not self.samples:
+            return None
+        return {"median": statistics.median(self.samples), "min": min(self.samples), "max": max(self.samples),
+                "samples": len(self.samples),
+                "source": "sysfs pp_dpm_sclk current level, every 20 ms during the timed decode steps"}
+
+
 def run_decode(args):
     dec = DecodeBench()
-    ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
+    with ClockSampler() as clk:
+        ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
     ms_call, ms_min, ms_med = time_launches(dec.step, max(args.steps, 20))
     err = dec.check()
     log(f"decode: sampled rows within {err:.2e} of the oracle")
@@ -636,6 +686,7 @@ def run_decode(args):
                      "avg_launch_us": round(ms_call * 1e3, 2), "min_launch_us": round(ms_min * 1e3, 2),
                      "median_launch_us": round(ms_med * 1e3, 2)},
         "oracle_max_rel_err": err,
+        "gpu_sclk_mhz": clk.summary(),
         "decode_window": run_window(dec, args),
         "page_runs": run_rows(dec, args),
     }
@@ -691,6 +742,21 @@ def run_sparse(args):
         if name != "pool_blocks":
             total_us += ms * 1e3
         log(f"sparse {name}: {ms * 1e3:.1f} us, {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    # dense decode of the same streams (every cached row), the bytes the selection avoids
+    import torch
+    P = sb.P
+    dws = torch.zeros(P.paged_attn_decode_workspace(sb.S, sb.HQ, sb.L), dtype=torch.uint8, device="cuda")
+    dout = torch.empty_like(sb.out)
+
+    def dense(i):
+        P.paged_attn_decode(sb.q, P.PAGED_BF16, sb.HQ, sb.kv, sb.pg, sb.lens, sb.S, sb.L, 1 / 16, dout, dws)
+    ms, _ = time_steps(dense, args.steps, args.warmup)
+    dbytes = sb.S * sb.HKV * sb.L * sb.D * 2 * 2 + sb.q.numel() * 2 + sb.S * (sb.L // sb.PTOK) * 4 + sb.S * 4 + dout.numel() * 4
+    sparse["dense_decode_131072"] = {"us": round(ms * 1e3, 2), "alg_bytes": dbytes,
+                                     "GB_per_s": round(dbytes / (ms * 1e-3) / 1e9, 1),
+                                     "hbm_frac": round(dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"dense decode over the same 3 x 131072 streams: {ms * 1e3:.1f} us, {dbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    del dws, dout
     ids_ok, serr = sb.check()
     sparse["decode_total_us"] = round(total_us, 2)
     sparse["topk_ids_equal_oracle"] = ids_ok
