@@ -27,10 +27,10 @@ def host_bytes(t: torch.Tensor) -> np.ndarray:
 class Placed:
     """A workload placed in one arena (paged, through its table) or contiguously (no table)."""
 
-    def __init__(self, w: Workload, paged: bool = True, guard: int = 4096, table=None):
+    def __init__(self, w: Workload, paged: bool = True, guard: int = 4096, table=None, cap=None):
         self.w = w
         self.paged = paged
-        cap = max(w.lens + [1])
+        cap = max(w.lens + [1]) if cap is None else cap  # positions a contiguous stream holds
         self.page_pos = w.page_pos if paged else cap
         self.table_np = (w.table if table is None else table) if paged else None
         self.olay = O.PageLayout(w.n_kv_heads, w.head_dim, self.page_pos, w.dtype, idx_dim=w.idx_dim)
