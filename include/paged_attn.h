@@ -208,7 +208,8 @@ int paged_pool_blocks(const void *ik, void *pooled, int32_t idx_dim, int32_t are
  *   qi         device [n_streams][n_idx_heads][idx_dim], qi_dtype
  *   pooled     device, pooled region base (float32 rows, see paged_pool_blocks);
  *              arena_dtype is the arena's K/V type, which gives page_elems its byte size
- *   out_scores optional device [n_streams][max_len/4] float64 (NULL: kept in workspace)
+ *   out_scores optional device [n_streams][max_len/4] float64 (NULL: kept in workspace); entries
+ *              past a stream's floor(L/4) blocks are not written
  *   workspace  >= paged_topk_workspace(n_streams, max_len, k) bytes, 16-byte aligned: per-stream
  *              coarse score histograms (4096 uint32), per 1024 blocks the selection counts,
  *              taken bits and candidate (key, id) pairs (12 KiB + 136 bytes) and, without
