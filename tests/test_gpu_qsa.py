@@ -353,3 +353,39 @@ def test_topk_stream_past_the_selection_bitmap():
     bitmap holds: the single-workgroup list path selects, bit for bit against the oracle."""
     w = make_workload(67, [1048580], 256, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=1)
     _topk_checked(w, Placed(w), 512)
+
+
+def test_scores_sum_order_matches_oracle():
+    """Indexer keys (1, 2^60, -2^60, 0, ...) in every row and queries chosen so that only one float64
+    accumulator run head by head, dim by dim gives the oracle's value (0, 0, 1 for the three
+    streams); any other order of the additions would give 1, 1, 1 or lose the 1."""
+    lens = [64, 64, 64]
+    w = make_workload(68, lens, 16, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=2)
+    big = 2.0 ** 60
+    IK = np.zeros(w.IK.shape, np.float32)
+    IK[:, :, 0], IK[:, :, 1], IK[:, :, 2] = 1.0, big, -big
+    w.IK = f32_to_bf16_bits(IK)
+    qI = np.zeros(w.qI.shape, np.float32)
+    qI[0, 0, :3] = 1.0                                  # one head: (1 + 2^60) - 2^60 = 0
+    qI[1, 0, 0], qI[1, 1, 1], qI[1, 1, 2] = 1.0, 1.0, 1.0  # head 0 then head 1: 0
+    qI[2, 0, 1], qI[2, 0, 2], qI[2, 1, 0] = 1.0, 1.0, 1.0  # heads swapped: 1
+    w.qI = f32_to_bf16_bits(qI)
+    pl = Placed(w)
+    S, ml, k = 3, 64, 4
+    b0 = dev(np.zeros(S, np.int32))
+    b1 = dev(np.array([L // 4 for L in lens], np.int32))
+    P.paged_pool_blocks(pl.ik, pl.pooled, 128, P.PAGED_BF16, pl.pg, b0, b1, S, ml)
+    ids = torch.empty((S, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(S, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((S, ml // 4), dtype=torch.float64, device="cuda")
+    ws = torch.empty(P.paged_topk_workspace(S, ml, k), dtype=torch.uint8, device="cuda")
+    P.paged_block_scores_topk(dev(w.qI), P.PAGED_BF16, 2, 128, pl.pooled, P.PAGED_BF16, pl.pg, pl.lens, S, ml, k,
+                              ids, cnt, sc, ws)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    assert np.all(sc[0] == 0.0) and np.all(sc[1] == 0.0) and np.all(sc[2] == 1.0)
+    pooled = O.pool(w.as_f64("IK"), lens)
+    for s in range(S):
+        assert np.array_equal(sc[s], O.scores(w.as_f64("qI")[s], pooled[s])), s
+    # ties everywhere: the first k ids
+    assert np.array_equal(ids.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (S, 1)))

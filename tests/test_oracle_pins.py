@@ -282,6 +282,22 @@ def test_scores_exact_on_integers_and_linear_in_heads():
     assert np.array_equal(O.scores(qs, pooled), got)
 
 
+def test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim():
+    """Terms chosen so that the order of the float64 additions decides the result: one accumulator
+    over head 0's dims, then head 1's, keeps 0; summing each head apart first, or the dims in
+    another order, keeps 1 (2^60 absorbs a 1 added after it, so only what precedes it is lost)."""
+    big = 2.0 ** 60
+    pooled = np.array([[1.0, big, -big]], np.float32)          # one block, 3 dims
+    # one head: 1 + 2^60 -> 2^60, then - 2^60 -> 0 (the dims in reverse order would give 1)
+    assert O.scores(np.array([[1.0, 1.0, 1.0]]), pooled)[0] == 0.0
+    # two heads: head 0 contributes only dim 0 (1), head 1 only dims 1, 2 (2^60, -2^60):
+    # one accumulator: (1 + 2^60) - 2^60 = 0; per-head sums first: 1 + (2^60 - 2^60) = 1
+    q2 = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 1.0]])
+    assert O.scores(q2, pooled)[0] == 0.0
+    # heads swapped: (0 + 2^60 - 2^60) + 1 = 1 in the stated order
+    assert O.scores(q2[::-1].copy(), pooled)[0] == 1.0
+
+
 def test_topk_matches_python_sort_and_ties():
     rng = np.random.default_rng(81)
     for trial in range(20):
