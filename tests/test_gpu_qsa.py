@@ -389,3 +389,22 @@ def test_scores_sum_order_matches_oracle():
         assert np.array_equal(sc[s], O.scores(w.as_f64("qI")[s], pooled[s])), s
     # ties everywhere: the first k ids
     assert np.array_equal(ids.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (S, 1)))
+
+
+def test_pool_sums_in_float64_and_rounds_once():
+    """Rows 1, 2^-24, 2^-24, 0 in dim 0 (and 2^20, 2^-20, -2^20, 2^-21 in dim 1): summed exactly and
+    rounded once they pool to 0.25 + 2^-25 (and (2^-20 + 2^-21) / 4); rounding after each float32
+    addition would give 0.25 (and 2^-21 / 4)."""
+    w = make_workload(69, [16], 16, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=8, n_idx_heads=1)
+    IK = np.zeros(w.IK.shape, np.float32)
+    IK[0, 0:4, 0] = [1.0, 2.0 ** -24, 2.0 ** -24, 0.0]
+    IK[0, 0:4, 1] = [2.0 ** 20, 2.0 ** -20, -(2.0 ** 20), 2.0 ** -21]
+    w.IK = f32_to_bf16_bits(IK)
+    pl = Placed(w)
+    b0, b1 = dev(np.zeros(1, np.int32)), dev(np.array([4], np.int32))
+    P.paged_pool_blocks(pl.ik, pl.pooled, 8, P.PAGED_BF16, pl.pg, b0, b1, 1, 16)
+    torch.cuda.synchronize()
+    got = _pooled_gpu(pl)[0]
+    assert got[0, 0] == np.float32(0.25 + 2.0 ** -25) and got[0, 0] != np.float32(0.25)
+    assert got[0, 1] == np.float32((2.0 ** -20 + 2.0 ** -21) / 4)
+    assert np.array_equal(got.view(np.uint32), O.pool(w.as_f64("IK"), [16])[0].view(np.uint32))
