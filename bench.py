@@ -666,6 +666,39 @@ class ClockSampler:
                 "source": "sysfs pp_dpm_sclk current level, every 20 ms during the timed decode steps"}
 
 
+def run_page_pool():
+    """The host page pool (no GPU): a pool of 65,536 pages; alloc then free of n pages in one call each,
+    and claim then release of a run of k pages, repeated; pages (or runs) handled per second and the
+    time per call pair, ctypes calls included."""
+    import numpy as np
+    import paged_kv_cache_pg_amd as P
+    n_pages = 65536
+    state = np.zeros(P.paged_pool_state_bytes(n_pages), np.uint8)
+    P.paged_pool_init(state, n_pages)
+    out = {}
+    for n in (1, 64, 1024):
+        pages = np.zeros(n, np.int32)
+        reps = max(200, 200000 // n)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            P.paged_pool_alloc(state, n, pages)
+            P.paged_pool_free(state, pages, n)
+        dt = time.perf_counter() - t0
+        out[f"alloc_free_{n}"] = {"us_per_pair": round(dt / reps * 1e6, 3), "pages_per_s": round(reps * n / dt, 1)}
+    for k in (4, 64):
+        reps = 20000
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            first = P.paged_pool_claim_run(state, k)
+            P.paged_pool_release_run(state, first, k)
+        dt = time.perf_counter() - t0
+        out[f"claim_release_run_{k}"] = {"us_per_pair": round(dt / reps * 1e6, 3)}
+    assert P.paged_pool_free_count(state) == n_pages
+    log(f"page pool: alloc+free of 1024 pages {out['alloc_free_1024']['us_per_pair']} us, "
+        f"claim+release of a 64-page run {out['claim_release_run_64']['us_per_pair']} us")
+    return out
+
+
 def run_decode(args):
     dec = DecodeBench()
     with ClockSampler() as clk:
@@ -813,6 +846,7 @@ def main():
         torch.cuda.empty_cache()
     if args.only in (None, "append"):
         result["append"] = run_append(args)
+        result["page_pool"] = run_page_pool()
         torch.cuda.empty_cache()
     if args.only is None and not args.no_cpu_baseline:
         result["cpu_baseline"] = DecodeBench.cpu_baseline_from_scratch()

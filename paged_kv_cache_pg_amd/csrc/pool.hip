@@ -8,7 +8,10 @@
 // caller's duty: nothing here touches the GPU).
 //
 // State (host memory the caller owns, paged_pool_state_bytes(n) bytes):
-//   header | stack[n] int32 (free page ids; the top of the stack is stack[n_free-1]) | kind[n] uint8
+//   header | below[n] int32 | above[n] int32 | kind[n] uint8
+// The free pages form a stack kept as a doubly linked list: below[p] / above[p] are the free pages
+// under and over p (-1 at the ends), header.top the page handed out next.  Taking a run's pages out
+// of the middle of the stack then costs k steps and keeps the order of the rest.
 // kind: 0 free, 1 handed out as a page, 2 part of a run (3 marks a page while a free list is checked).
 #include <stdint.h>
 #include <string.h>
@@ -17,25 +20,28 @@
 
 namespace {
 
-constexpr uint32_t POOL_MAGIC = 0x4c504750u;  // "PGPL"
+constexpr uint32_t POOL_MAGIC = 0x4c504751u;  // "QGPL"
 
 struct PoolHeader {
   uint32_t magic;
   int32_t n_pages;
   int32_t n_free;
+  int32_t top;     // free page on top of the stack, -1 when none
+  int32_t bottom;  // free page at the bottom of the stack, -1 when none
   int32_t reserved;
 };
 
 enum : uint8_t { KIND_FREE = 0, KIND_PAGE = 1, KIND_RUN = 2, KIND_MARK = 3 };
 
 size_t state_bytes(int64_t n) {
-  const size_t b = sizeof(PoolHeader) + (size_t)n * sizeof(int32_t) + (size_t)n;
+  const size_t b = sizeof(PoolHeader) + (size_t)n * 2 * sizeof(int32_t) + (size_t)n;
   return (b + 7) & ~(size_t)7;
 }
 
 struct View {
   PoolHeader* h;
-  int32_t* stack;
+  int32_t* below;
+  int32_t* above;
   uint8_t* kind;
 };
 
@@ -44,9 +50,29 @@ bool view_of(void* state, View* v) {
   PoolHeader* h = (PoolHeader*)state;
   if (h->magic != POOL_MAGIC || h->n_pages < 1 || h->n_free < 0 || h->n_free > h->n_pages) return false;
   v->h = h;
-  v->stack = (int32_t*)(h + 1);
-  v->kind = (uint8_t*)(v->stack + h->n_pages);
+  v->below = (int32_t*)(h + 1);
+  v->above = v->below + h->n_pages;
+  v->kind = (uint8_t*)(v->above + h->n_pages);
   return true;
+}
+
+void push(View& v, int32_t p) {
+  v.below[p] = v.h->top;
+  v.above[p] = -1;
+  if (v.h->top >= 0) v.above[v.h->top] = p;
+  else v.h->bottom = p;
+  v.h->top = p;
+  v.kind[p] = KIND_FREE;
+  ++v.h->n_free;
+}
+
+void unlink(View& v, int32_t p) {
+  const int32_t b = v.below[p], a = v.above[p];
+  if (b >= 0) v.above[b] = a;
+  else v.h->bottom = a;
+  if (a >= 0) v.below[a] = b;
+  else v.h->top = b;
+  --v.h->n_free;
 }
 
 }  // namespace
@@ -66,11 +92,16 @@ int paged_pool_init(void* state, size_t state_size, int32_t n_pages) {
   h->n_pages = n_pages;
   h->n_free = n_pages;
   h->reserved = 0;
-  int32_t* stack = (int32_t*)(h + 1);
-  uint8_t* kind = (uint8_t*)(stack + n_pages);
+  View v;
+  view_of(state, &v);
   // page 0 on top: pages come off the stack from the bottom of the arena up
-  for (int32_t i = 0; i < n_pages; ++i) stack[i] = n_pages - 1 - i;
-  memset(kind, KIND_FREE, (size_t)n_pages);
+  for (int32_t p = 0; p < n_pages; ++p) {
+    v.below[p] = p + 1 < n_pages ? p + 1 : -1;
+    v.above[p] = p - 1;
+  }
+  h->top = 0;
+  h->bottom = n_pages - 1;
+  memset(v.kind, KIND_FREE, (size_t)n_pages);
   return PAGED_OK;
 }
 
@@ -85,7 +116,8 @@ int paged_pool_alloc(void* state, int32_t n, int32_t* pages) {
   if (!view_of(state, &v) || n < 0 || (n > 0 && pages == nullptr)) return PAGED_EINVAL;
   if (n > v.h->n_free) return PAGED_EFULL;  // nothing is taken: the request waits
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t p = v.stack[--v.h->n_free];
+    const int32_t p = v.h->top;
+    unlink(v, p);
     v.kind[p] = KIND_PAGE;
     pages[i] = p;
   }
@@ -106,10 +138,7 @@ int paged_pool_free(void* state, const int32_t* pages, int32_t n) {
     for (int32_t j = 0; j < i; ++j) v.kind[pages[j]] = KIND_PAGE;
     return PAGED_EINVAL;
   }
-  for (i = 0; i < n; ++i) {
-    v.kind[pages[i]] = KIND_FREE;
-    v.stack[v.h->n_free++] = pages[i];
-  }
+  for (i = 0; i < n; ++i) push(v, pages[i]);
   return PAGED_OK;
 }
 
@@ -126,14 +155,11 @@ int paged_pool_claim_run(void* state, int32_t k, int32_t* first) {
     }
   }
   if (found < 0) return PAGED_EFULL;  // too fragmented for the run: the request waits
-  for (int32_t p = found; p < found + k; ++p) v.kind[p] = KIND_RUN;
-  // drop the run's pages from the free stack, keeping the order of the rest
-  int32_t w = 0;
-  for (int32_t i = 0; i < v.h->n_free; ++i) {
-    const int32_t p = v.stack[i];
-    if (v.kind[p] == KIND_FREE) v.stack[w++] = p;
+  // out of the free stack, the order of the rest kept
+  for (int32_t p = found; p < found + k; ++p) {
+    unlink(v, p);
+    v.kind[p] = KIND_RUN;
   }
-  v.h->n_free = w;
   *first = found;
   return PAGED_OK;
 }
@@ -144,10 +170,7 @@ int paged_pool_release_run(void* state, int32_t first, int32_t k) {
   for (int32_t p = first; p < first + k; ++p)
     if (v.kind[p] != KIND_RUN) return PAGED_EINVAL;
   // pushed from the top page down, so the run's lowest page comes off the stack first
-  for (int32_t p = first + k - 1; p >= first; --p) {
-    v.kind[p] = KIND_FREE;
-    v.stack[v.h->n_free++] = p;
-  }
+  for (int32_t p = first + k - 1; p >= first; --p) push(v, p);
   return PAGED_OK;
 }
 
