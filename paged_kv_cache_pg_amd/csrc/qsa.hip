@@ -98,22 +98,27 @@ __device__ __forceinline__ void widen_q(const TopkArgs& a, int s, double* s_q) {
   }
 }
 
-// 128-dim rows: n_idx_heads x 128 query values (at most 2048), 16 bytes a lane at a time, every
-// load issued before the first is used.
+// 128-dim rows: n_idx_heads x 128 query values (at most 2048), 16 bytes a lane at a time.  The
+// loads are issued by q128_load and widened into LDS by q128_store, so that the caller can put other
+// loads between them.  A chunk past the queries re-reads the last one (a uniform test skips the
+// rounds no lane needs) and is not stored.
+constexpr int SC_QCH = 2048 / 4 / SC_NB;  // 16-byte query chunks a lane at most
 template <bool QBF16>
-__device__ __forceinline__ void widen_q128(const TopkArgs& a, int s, double* s_q) {
+__device__ __forceinline__ void q128_load(const TopkArgs& a, int s, uint4 (&v)[SC_QCH]) {
   constexpr int PER = QBF16 ? 8 : 4;  // values a 16-byte chunk
   const int m = a.n_idx_heads * 128;
   const int nch = m / PER;
   const uint4* src = (const uint4*)((const char*)a.qi + (int64_t)s * m * (QBF16 ? 2 : 4));
-  uint4 v[2048 / 4 / SC_NB];
 #pragma unroll
-  for (int j = 0; j < 2048 / 4 / SC_NB; ++j) {
-    const int c = threadIdx.x + j * SC_NB;
-    if (c < nch) v[j] = src[c];
-  }
+  for (int j = 0; j < SC_QCH; ++j)
+    if (j * SC_NB < nch) v[j] = src[min((int)threadIdx.x + j * SC_NB, nch - 1)];
+}
+template <bool QBF16>
+__device__ __forceinline__ void q128_store(const TopkArgs& a, const uint4 (&v)[SC_QCH], double* s_q) {
+  constexpr int PER = QBF16 ? 8 : 4;
+  const int nch = a.n_idx_heads * 128 / PER;
 #pragma unroll
-  for (int j = 0; j < 2048 / 4 / SC_NB; ++j) {
+  for (int j = 0; j < SC_QCH; ++j) {
     const int c = threadIdx.x + j * SC_NB;
     if (c < nch) {
       const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -138,15 +143,27 @@ __global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
   __shared__ int64_t s_base[SC_NB];
   const int s = blockIdx.y, lane = threadIdx.x;
   if (blockIdx.x == 0) zero_hist(a, s);
-  // The table entries (every block below max_blocks has one) and the queries are read before the
-  // stream's length is known, so the three loads take one round trip; a lane's row base is used
-  // only for rows below the length.
+  // This lane's table entry (every block below max_blocks has one), the queries and the stream's
+  // length are all requested before any of them is used, so they take one round trip: the entry
+  // is read without a branch (from the length when there is no table, and then not used), and
+  // the length, which is wanted first, is requested last.  A lane's row base is used only for
+  // rows below the length.
   const int b0 = blockIdx.x * SC_NB;
   const int b = b0 + lane;
-  s_base[lane] = pool_at(a.pg, s, min(b, a.max_blocks - 1), 128 * 4);
-  widen_q128<QBF16>(a, s, s_q);
-  const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
+  const bool paged = a.pg.table != nullptr;
+  const int p = 4 * min(b, a.max_blocks - 1);
+  const uint32_t lp = (uint32_t)p / (uint32_t)a.pg.ptok;
+  const int32_t* tp = paged ? a.pg.table + (int64_t)s * a.pg.stride + lp : a.lens + s;
+  const int32_t entry = *tp;
+  uint4 qv[SC_QCH];
+  q128_load<QBF16>(a, s, qv);
+  const int len = a.lens[s];
+  const int nb = min(max(len, 0), a.max_blocks * 4) >> 2;
   if (b0 >= nb) return;
+  const int64_t page = paged ? (int64_t)entry : (int64_t)s;
+  const int within = paged ? p - (int)lp * a.pg.ptok : p;
+  s_base[lane] = page * a.pg.page_bytes + (int64_t)(within >> 2) * (128 * 4);
+  q128_store<QBF16>(a, qv, s_q);
   const int nrows = min(SC_NB, nb - b0);
   __syncthreads();
 
