@@ -30,6 +30,16 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(B._SIGS), "binding and header disagree"
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no other path to fall back on."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libpagedattn.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        P.strerror(0)
+    with pytest.raises(RuntimeError, match="missing"):
+        P.paged_attn_decode_workspace(4, 32, 40960)
+
+
 def test_strerror():
     assert P.strerror(0) == "ok"
     assert "workspace" in P.strerror(-3)
