@@ -43,19 +43,31 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #ifndef PAGED_PF_PV_AHEAD
 #define PAGED_PF_PV_AHEAD 4         // V^T fragment reads (pairs) ahead of their MFMAs
 #endif
+#ifndef PAGED_PF_ROWS
+#define PAGED_PF_ROWS 128           // (query, head) rows a workgroup
+#endif
+#ifndef PAGED_PF_KT
+#define PAGED_PF_KT 64              // keys a tile (a multiple of 32)
+#endif
+#ifndef PAGED_PF_WG_PER_CU
+#define PAGED_PF_WG_PER_CU 1        // workgroups a CU the register budget is set for
+#endif
 constexpr int RB = PAGED_PF_RB;
-constexpr int PF_ROWS = 128;        // (query, head) rows a workgroup
+constexpr int PF_ROWS = PAGED_PF_ROWS;
 constexpr int PF_WAVES = PF_ROWS / (16 * RB);
 constexpr int PF_THREADS = 64 * PF_WAVES;
-constexpr int PF_KT = 64;           // keys a tile
+constexpr int PF_KT = PAGED_PF_KT;
+constexpr int KB = PF_KT / 16;      // 16-key blocks of S^T a tile
+constexpr int NS2 = PF_KT / 32;     // 32-key PV steps a tile
 constexpr int ROWB = HD * 2;        // bytes a bf16 key / value row
 constexpr int CH = ROWB / 16;       // 16-byte chunks a row (32)
 constexpr int TILEB = PF_KT * ROWB; // bytes a K or V tile in LDS (rows unpadded, chunks swizzled)
-constexpr int LD_PER_WAVE = PF_KT * CH / PF_THREADS;  // 1 KB global->LDS loads a wave a tile (8)
+constexpr int LD_PER_WAVE = PF_KT * CH / PF_THREADS;  // 1 KB global->LDS loads a wave a tile
+static_assert(PF_KT % 32 == 0 && PF_KT * CH % PF_THREADS == 0, "tile shape");
 constexpr float RESCALE_SLACK = 8.f;  // log2 units a row's running max may lag behind before O is rescaled
 
 template <int G>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
+__global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel(PreArgs a) {
   constexpr int QB = PF_ROWS / G;  // queries a workgroup
   __shared__ __attribute__((aligned(16))) char s_k[2][TILEB];
   __shared__ __attribute__((aligned(16))) char s_v[2][TILEB];
@@ -145,24 +157,24 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
   // in order.  Steps run ds-major so that the 8 accumulators take turns (a dependent MFMA is
   // 8 issues behind its predecessor); the K fragment of step (ds, kb) is read QK_AHEAD steps
   // before its two MFMAs.
-  auto qk = [&](const char* kbuf, f32x4 (&sacc)[4][RB]) {
+  auto qk = [&](const char* kbuf, f32x4 (&sacc)[KB][RB]) {
     constexpr int QK_AHEAD = PAGED_PF_QK_AHEAD;
     auto kfrag = [&](int st) {
-      const int ds = st >> 2, kb = st & 3;
+      const int ds = st / KB, kb = st % KB;
       return *(const bf16x8*)(kbuf + koff[ds] + 16 * ROWB * kb);
     };
     bf16x8 ring[QK_AHEAD];
 #pragma unroll
     for (int st = 0; st < QK_AHEAD; ++st) ring[st] = kfrag(st);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 32; ++st) {
+    for (int st = 0; st < 8 * KB; ++st) {
       const bf16x8 kf = ring[st % QK_AHEAD];
-      if (st + QK_AHEAD < 32) ring[st % QK_AHEAD] = kfrag(st + QK_AHEAD);
-      const int ds = st >> 2, kb = st & 3;
+      if (st + QK_AHEAD < 8 * KB) ring[st % QK_AHEAD] = kfrag(st + QK_AHEAD);
+      const int ds = st / KB, kb = st % KB;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][ds], sacc[kb][rb], 0, 0, 0);
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     // keep one fragment read a step: reads QK_AHEAD steps ahead, two MFMAs a step
     __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
 #pragma unroll
-    for (int st = 0; st < 32 - QK_AHEAD; ++st) {
+    for (int st = 0; st < 8 * KB - QK_AHEAD; ++st) {
       __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -206,21 +218,21 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
     stage_keyat(t + 2, page_next);
     page_next = key_page(t + 3);
 
-    f32x4 s_cur[4][RB];
+    f32x4 s_cur[KB][RB];
     qk(s_k[t & 1], s_cur);
 
-    bf16x8 phi[2][RB], plo[2][RB];  // [32-key step][rb]
+    bf16x8 phi[NS2][RB], plo[NS2][RB];  // [32-key step][rb]
     float alpha_rb[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       // A tile every row of the block sees whole (below the diagonal) takes no mask, and its
       // scores are finite, so exp2 needs no -inf test: one multiply, max, subtract, exp2 and add a score.
       const bool full = __all(k0 + PF_KT <= lim[rb]);
-      float z[4][4];
+      float z[KB][4];
       float mx = NEG_INF;
       if (full) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             z[kb][i] = s_cur[kb][rb][i] * a.zscale;
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = k0 + 16 * kb + 4 * u + i;
@@ -244,10 +256,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
       const float alpha = !move ? 1.f : (m_run[rb] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
       alpha_rb[rb] = alpha;
       float rs = 0.f;
-      float p[4][4];
+      float p[KB][4];
       if (full) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             p[kb][i] = __builtin_amdgcn_exp2f(z[kb][i] - m_new);
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             p[kb][i] = (z[kb][i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(z[kb][i] - m_new);
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
       m_run[rb] = m_new;
       // P^T fragment of 32-key step s2: element e is key 32s2 + 16(e/4) + 4u + e%4
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < NS2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pv = {p[2 * s2 + (e >> 2)][e & 3], p[2 * s2 + (e >> 2)][(e & 3) + 1]};
@@ -312,10 +324,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) ring[st][e] = vfrag(st >> 3, 2 * (st & 7) + e);
 #pragma unroll
-      for (int st = 0; st < 16; ++st) {
+      for (int st = 0; st < 8 * NS2; ++st) {
         const int s2 = st >> 3, db0 = 2 * (st & 7);
         bf16x8 vf[2] = {ring[st % PV_AHEAD][0], ring[st % PV_AHEAD][1]};
-        if (st + PV_AHEAD < 16) {
+        if (st + PV_AHEAD < 8 * NS2) {
           const int sn = st + PV_AHEAD;
 #pragma unroll
           for (int e = 0; e < 2; ++e) ring[st % PV_AHEAD][e] = vfrag(sn >> 3, 2 * (sn & 7) + e);
@@ -333,7 +345,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PreArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 4 * PV_AHEAD, 0);
 #pragma unroll
-      for (int st = 0; st < 16 - PV_AHEAD; ++st) {
+      for (int st = 0; st < 8 * NS2 - PV_AHEAD; ++st) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
