@@ -809,7 +809,7 @@ def main():
                     help="run one row only (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -71,7 +71,7 @@ typedef enum { PAGED_F32 = 0, PAGED_BF16 = 1, PAGED_FP8_E4M3 = 2 } paged_dtype;
 enum {
   PAGED_OK = 0,
   PAGED_EINVAL = -1,       /* an argument is out of range, NULL or misaligned  */
-  PAGED_EUNSUPPORTED = -2, /* a valid request this build does not serve        */
+  PAGED_EUNSUPPORTED = -2, /* a valid request this library does not serve      */
   PAGED_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
   PAGED_EHIP = -4,         /* a HIP launch failed                               */
   PAGED_EFULL = -5         /* no free page or run: the request waits (page pool) */
@@ -99,7 +99,7 @@ typedef struct {
   const void *v;         /* device, 16-byte aligned: the V region of page 0, same shape              */
   int32_t dtype;         /* paged_dtype of K and V                                                     */
   int32_t n_kv_heads;    /* Hkv >= 1                                                                   */
-  int32_t head_dim;      /* D; this build serves D = 256                                               */
+  int32_t head_dim;      /* D; the library serves D = 256                                              */
   int32_t reserved;      /* must be 0                                                                  */
   const void *k_scale;   /* PAGED_FP8_E4M3: device, 4-byte aligned, K scale region of page 0           */
   const void *v_scale;   /* PAGED_FP8_E4M3: device, 4-byte aligned, V scale region of page 0           */

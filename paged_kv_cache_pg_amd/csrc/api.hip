@@ -422,7 +422,7 @@ const char* paged_strerror(int status) {
   switch (status) {
     case PAGED_OK: return "ok";
     case PAGED_EINVAL: return "invalid argument";
-    case PAGED_EUNSUPPORTED: return "unsupported by this build";
+    case PAGED_EUNSUPPORTED: return "unsupported by this library";
     case PAGED_EWORKSPACE: return "workspace missing or too small";
     case PAGED_EHIP: return "HIP launch failed";
     case PAGED_EFULL: return "no free page or run (the request waits)";

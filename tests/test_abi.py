@@ -207,3 +207,15 @@ def test_window_refusals():
     assert win(2, ws=0) == B.PAGED_EWORKSPACE
     # workspace rows scale with the window
     assert P.paged_attn_decode_window_workspace(4, 32, 2, 40960) == 2 * P.paged_attn_decode_workspace(4, 32, 40960)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits with a message, before touching a device."""
+    import subprocess
+    import sys
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, (argv, r.returncode, r.stderr[-500:])
+        assert "one GPU" in r.stderr
+        assert r.stdout == ""
