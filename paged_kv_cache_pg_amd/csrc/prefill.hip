@@ -41,7 +41,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define PAGED_PF_QK_AHEAD 4         // K fragment reads ahead of their MFMAs
 #endif
 #ifndef PAGED_PF_PV_AHEAD
-#define PAGED_PF_PV_AHEAD 4         // V^T fragment reads (pairs) ahead of their MFMAs
+#define PAGED_PF_PV_AHEAD 8         // V^T fragment reads (pairs) ahead of their MFMAs
 #endif
 #ifndef PAGED_PF_ROWS
 #define PAGED_PF_ROWS 128           // (query, head) rows a workgroup
