@@ -302,7 +302,10 @@ constexpr int TK_BINS = 4096;       // coarse bins
 constexpr int TK_CMAX = 4096;       // candidates ranked in LDS
 constexpr int TK_AMAX = 8192;       // k at most for the list path
 constexpr int TK_BATCH = 16;        // score chunks a thread reads at once
-constexpr int HK_ITEMS = 1024;      // scores a histogram workgroup
+#ifndef PAGED_HK_ITEMS
+#define PAGED_HK_ITEMS 1024
+#endif
+constexpr int HK_ITEMS = PAGED_HK_ITEMS;  // scores a histogram workgroup
 constexpr int SEL_ITEMS = 1024;     // blocks a selection workgroup
 constexpr int SEL_THREADS = 256;
 constexpr int TK_SBITS = 1 << 18;   // blocks a stream whose selected candidates are marked in LDS
