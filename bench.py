@@ -33,10 +33,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
 DECODE_TRAFFIC_BYTES = 676_357_492
-DECODE_TRAFFIC_SOURCES = "a7848aa08d370ba9"
+DECODE_TRAFFIC_SOURCES = "45502037ee3659c5"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
 FP8_TRAFFIC_BYTES = 346_334_423
-FP8_TRAFFIC_SOURCES = "175b3b95cbc3e098"
+FP8_TRAFFIC_SOURCES = "3e1d85c67aecfe95"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")
@@ -46,11 +46,18 @@ _FP8_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode_mfma.hip", "paged_kv_cache_pg
 
 
 def _sources_hash(files=_DECODE_SOURCES) -> str:
+    """Hash of the kernels' code: comments dropped and whitespace collapsed, so that only a change
+    to the code itself invalidates a traffic figure."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -13,19 +13,20 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Page table (the pages' Pg argument, [P1 "What this changes"]): an int page
- * table, the elements in a page and the positions in a page.  The row of
+ * Page table (the pages' Pg argument, [P1 "What this changes"]): three values
+ * describe paging, the int table itself and how many elements and positions a
+ * page holds.  The row of
  * (stream s, head h, position p) in a region whose page part is
  * [H][page_pos][W] starts at element
  *     table[s * table_stride + p / page_pos] * page_elems + (h * page_pos + p % page_pos) * W
  * and, with no table (table == NULL), at the old contiguous expression
  *     s * page_elems + (h * cap + p) * W       with page_pos = cap,
- * i.e. each stream keeps "cap rows a head" ([P2 commit 3f5b87d]).  page_elems
+ * i.e. each stream reserves cap rows per head ([P2 commit 3f5b87d]).  page_elems
  * counts elements of the arena's K/V type; a float32 pooled row in a bf16
  * arena uses two slots per value.
  *
- * Region bases: a cache pointer is its layer's part of page 0 ([P1 "What this
- * changes"]); k, v, ik and pooled are such pointers into one arena.
+ * Region bases: each cache pointer addresses the share of page 0 that belongs to
+ * its layer ([P1 "What this changes"]); k, v, ik and pooled are such pointers into one arena.
  *
  * Ownership ([P2 maintainer replies: drain before anything is freed, fills on
  * the engine stream]): the caller allocates and owns every buffer (inputs,
@@ -37,8 +38,8 @@
  *
  * Errors: a negative status is returned before anything is enqueued when an
  * argument is refused (the pages refuse what they cannot serve: a page size
- * that is not a multiple of 4 [P2 "What this changes"], a run shorter than its
- * parts [P2 commit 51f8354]).  PAGED_EHIP reports a failed launch.  Table
+ * that does not divide by 4 [P2 "What this changes"], a run with fewer pages
+ * than its parts need [P2 commit 51f8354]).  PAGED_EHIP reports a failed launch.  Table
  * entries are not range-checked on the device: an entry outside the arena is
  * undefined behaviour.  Lengths, block ranges and block ids are clamped or
  * ignored on the device as stated per call, so that no table entry past the
@@ -46,9 +47,9 @@
  *
  * Numerics: every sum keeps one fixed order that depends only on a stream's
  * own length (never on the page size, the table or the other streams), so the
- * paged result is byte-equal to the contiguous one at any page size that holds
- * whole rows ([P1 "What this changes": "Only addresses change; no sum changes
- * order"]), and a stream in a batch equals the same stream alone.
+ * paged result is byte-equal to the contiguous one for every page size made of
+ * whole rows ([P1 "What this changes": paging alters where rows are read, never
+ * the order of a sum]), and a stream in a batch equals the same stream alone.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -63,8 +64,8 @@ extern "C" {
 
 /* Element types.  PAGED_FP8_E4M3 rows are 256 e4m3 codes (OCP E4M3: 1 sign, 4 exponent bits with
    bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448) that stand for
-   code x scale with one float32 scale a row ([P2 commit 5c09685]: a row's e4m3 codes and fp32
-   scale, read through the row's page).  Only the K/V regions of an attention layer take this type. */
+   code x scale with one float32 scale a row ([P2 commit 5c09685]: each row's fp8 codes and its
+   float32 scale are reached via the page holding the row).  Only the K/V regions of an attention layer take this type. */
 typedef enum { PAGED_F32 = 0, PAGED_BF16 = 1, PAGED_FP8_E4M3 = 2 } paged_dtype;
 
 /* Status codes. */
@@ -89,8 +90,8 @@ typedef struct {
 
 /* Key and value regions of one attention layer ([P2 commit 3f5b87d]:
    [key, value][head][position][row] inside a page).
-   PAGED_FP8_E4M3 ([P2 commit 5c09685]; page_elems then counts bytes, the pages' page size "in bytes
-   for fp8"): k and v hold the codes, [Hkv][page_pos][256] bytes a page, and k_scale / v_scale the
+   PAGED_FP8_E4M3 ([P2 commit 5c09685]; page_elems then counts bytes, as the pages size an fp8 page in
+   bytes): k and v hold the codes, [Hkv][page_pos][256] bytes a page, and k_scale / v_scale the
    rows' float32 scales, [Hkv][page_pos] a page, addressed like rows of 4 bytes:
      scale of (s, h, p) at byte  table[s * table_stride + p / page_pos] * page_elems + (h * page_pos + p % page_pos) * 4
    from k_scale (v_scale).  The scale fields are read only when dtype == PAGED_FP8_E4M3. */
@@ -106,8 +107,9 @@ typedef struct {
 } paged_kv;
 
 /* ------------------------------------------------------------------------ */
-/* Dense decode ([P1 "What this changes": fn_attn_chunks' key and value tiles
- * read through pg_at, one lookup per key per tile, key_at beside key_ids;
+/* Dense decode ([P1 "What this changes": fn_attn_chunks gets its key and value
+ * tiles via pg_at, resolving each key's row a single time per tile and keeping
+ * key_at in shared memory next to key_ids;
  * P2 commit ce5b78d: attention partials]).
  *
  * For every stream s and query head h: out[s][h] = softmax(scale * K q) V over
@@ -159,7 +161,8 @@ size_t paged_attn_decode_window_workspace(int32_t n_streams, int32_t n_q_heads, 
 
 /* ------------------------------------------------------------------------ */
 /* Chunked causal prefill for one stream ([P2 maintainer reply: paged or mixed
- * prompt batches take the page-run path, flat ones the tensor-core attention;
+ * prompts read from paged caches go down the page-run path and flat ones use
+ * tensor-core attention;
  * here one MFMA kernel serves both through pg_at]).
  *
  * Queries at absolute positions q_pos0 .. q_pos0+n_q-1 attend, per head, to the
@@ -244,9 +247,9 @@ int paged_sparse_attn(const void *q, int32_t q_dtype, int32_t n_q_heads,
 size_t paged_sparse_attn_workspace(int32_t n_streams, int32_t n_q_heads, int32_t k);
 
 /* ------------------------------------------------------------------------ */
-/* Row stores and gathers ([P1 "What this changes": fn_attn_prep stores keys,
- * values and indexer keys through pg_at; prompt-cache saves and restores copy
- * page runs in the contiguous layout]).
+/* Row stores and gathers ([P1 "What this changes": fn_attn_prep writes keys,
+ * values and indexer keys at pg_at addresses; a saved or restored prompt cache
+ * moves runs of pages to and from the contiguous layout]).
  *
  * paged_rows_store copies rows (s, h, p) for p in [pos_begin[s], pos_end[s])
  * (clamped to [0, max_len)) and h < n_heads from a strided source into a
@@ -283,7 +286,7 @@ int paged_rows_gather(void *dst, int64_t stride_s, int64_t stride_h, int64_t str
  *                ik, pooled and idx_dim are ignored)
  *   kv           K and V region bases; ik, pooled: region bases as for paged_pool_blocks
  *   pos0         device [n_streams] int32
- * page_pos must be a multiple of 4 when ik_new is given.  The caller must not run two
+ * page_pos must divide by 4 when ik_new is given.  The caller must not run two
  * appends that write the same rows concurrently.
  *
  * e4m3 arenas (kv->dtype == PAGED_FP8_E4M3, [P2 commit 5c09685]: the fp8 store takes a row's
@@ -310,11 +313,12 @@ int paged_row_offsets(const paged_pg *pg, int32_t n_streams, int32_t row_width,
                       int64_t *out, int32_t n, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* Host page pool ([P2 commit 1ac2075]: the free stack hands out KV pages from
- * the bottom; findRun / claimRun / releaseRun take k consecutive free pages
- * from the top; a pool too fragmented for a run makes the request wait.
- * [P2 description]: a lane's pages and run go back once the engine's stream
- * drains -- the caller's duty; nothing here touches the GPU).
+/* Host page pool ([P2 commit 1ac2075]: single KV pages come off a free stack
+ * that starts at the low end of the arena; findRun / claimRun / releaseRun take
+ * k adjacent free pages at the high end; when fragmentation leaves no such run
+ * the request has to wait.  [P2 description]: pages and runs are returned only
+ * after the engine's stream has drained -- the caller's duty; nothing here
+ * touches the GPU).
  *
  * The pool lives in host memory the caller owns and passes to every call:
  * paged_pool_state_bytes(n_pages) bytes, 8-byte aligned, set up by

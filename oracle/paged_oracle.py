@@ -52,9 +52,9 @@ ESIZE = {"bf16": 2, "f32": 4, "fp8": 1}
 class PageLayout:
     """Where each region of one attention layer sits inside a page.
 
-    [P1 "What this changes"]: a page of n positions holds, for each attention
-    layer, the keys, values and indexer keys of its n positions and the pooled
-    rows of their n/4 blocks.  [P2 commit 3f5b87d]: inside a page the order is
+    [P1 "What this changes"]: each page covers n positions; per attention layer
+    it stores their keys, values and indexer keys, plus one pooled row for each
+    of their n/4 blocks.  [P2 commit 3f5b87d]: inside a page the order is
     [key, value][head][position][row].  Reading taken: K [Hkv][n][D], then
     V [Hkv][n][D], then IK [n][DI], then POOL [n/4][DI] float32.
     All offsets are in bytes.
@@ -122,10 +122,10 @@ def row_offset(table, page_pos: int, page_elems: int, s: int, h: int, p: int, wi
     """Element offset of row (stream s, head h, position p) in a region whose page part is
     [H][rows_per_head][width].
 
-    [P1 "What this changes"]: with no table the old contiguous expression; with a
-    table the start of the page that holds the position plus the row inside that
-    page.  [P2 commit 3f5b87d]: with no table a stream keeps "cap rows a head",
-    which is this same expression with page_pos = cap and the implicit table [s].
+    [P1 "What this changes"]: without a table the earlier contiguous formula;
+    with one, the base of the page containing the position plus the row's offset
+    within it.  [P2 commit 3f5b87d]: without a table each stream reserves cap rows
+    per head, which is this same expression with page_pos = cap and the implicit table [s].
     """
     if rows_per_head is None:
         rows_per_head = page_pos
@@ -142,7 +142,7 @@ def pool_row_offset(table, page_pos: int, page_elems_f32: int, s: int, b: int, w
     """Float32-element offset of the pooled row of block b (positions 4b..4b+3).
 
     The block's rows share one page because page_pos is a multiple of 4
-    ([P2 "What this changes"]: n must be a multiple of 4); its pooled row is
+    ([P2 "What this changes"]: the positions a page holds must divide by 4); its pooled row is
     row (4b mod n)/4 of that page's POOL region.
     """
     p = 4 * b
@@ -408,8 +408,8 @@ def e4m3_value(codes) -> np.ndarray:
     bits 6..3 the exponent with bias 7, bits 2..0 the mantissa.  An exponent
     field of 0 is subnormal, m/8 * 2^-6; otherwise (1 + m/8) * 2^(e-7).
     S.1111.111 is NaN; there are no infinities, so S.1111.110 = 448 is the
-    largest magnitude.  [P2 commit 5c09685]: rows are e4m3 codes and the
-    reference dequantizes e4m3 x scale in float64.
+    largest magnitude.  [P2 commit 5c09685]: rows hold e4m3 codes, and
+    the check computes each value as code times scale in float64.
     """
     c = np.asarray(codes).astype(np.int64) & 0xFF
     sign = np.where(c & 0x80, -1.0, 1.0)

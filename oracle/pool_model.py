@@ -1,9 +1,10 @@
 """Plain model of the host page pool -- TEST INFRASTRUCTURE ONLY (tests/ may use it;
 nothing on the product path imports it).  It shares no code with the library.
 
-[P2] TensorFold PR #1170, commit 1ac2075: "the free stack hands out KV pages from
-the bottom"; findRun / claimRun / releaseRun "take k consecutive free pages from
-the top"; "a pool too fragmented for a run makes the request wait".
+[P2] TensorFold PR #1170, commit 1ac2075: single pages leave a free stack from the
+low end of the arena; findRun / claimRun / releaseRun take runs of k adjacent free
+pages from the high end; a request that finds no such run, the pool being too
+fragmented, waits.
 
 Readings where the pages are silent:
   * the free stack is last-in first-out, and a fresh pool hands out page 0, then

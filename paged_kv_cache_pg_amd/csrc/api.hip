@@ -33,7 +33,7 @@ int check_pg(const paged_pg* pg, int32_t dtype, int64_t max_len, bool need4) {
   if ((pg->page_elems * esize(dtype)) % 16 != 0) return PAGED_EINVAL;
   if (pg->table != nullptr) {
     if (!al(pg->table, 4) || pg->table_stride < 1) return PAGED_EINVAL;
-    if ((int64_t)pg->table_stride * pg->page_pos < max_len) return PAGED_EINVAL;  // a run shorter than its parts
+    if ((int64_t)pg->table_stride * pg->page_pos < max_len) return PAGED_EINVAL;  // the run has fewer pages than max_len needs
   } else {
     if ((int64_t)pg->page_pos < max_len) return PAGED_EINVAL;  // cap rows a head must cover max_len
   }

@@ -1,8 +1,8 @@
 // Device-side row addressing shared by every kernel of libpagedattn.
 //
-// pg_at follows TensorFold PR #1169 "What this changes": with no table a row is
-// the old contiguous expression; with a table it is the start of the page that
-// holds the position plus the row inside that page.  One uniform branch on the
+// pg_at follows TensorFold PR #1169 "What this changes": without a table a row
+// sits where the earlier contiguous formula puts it; with one, at the base of the
+// page containing the position plus the row's offset within that page.  One uniform branch on the
 // table pointer is the only difference between the two forms.
 #pragma once
 
@@ -31,7 +31,7 @@ __device__ __forceinline__ int64_t pg_offset(const PgDev& pg, int32_t page, int 
   return (int64_t)page * pg.page_bytes + ((int64_t)h * pg.ptok + within) * (int64_t)row_bytes;
 }
 
-// Byte offset of row (s, h, p): the start of the page that holds the position plus the row inside it.
+// Byte offset of row (s, h, p): base of the page containing position p, plus the row's offset in it.
 __device__ __forceinline__ int64_t pg_at(const PgDev& pg, int s, int h, int p, int row_bytes) {
   return pg_offset(pg, pg_page(pg, s, p), h, p, row_bytes);
 }

@@ -1,8 +1,8 @@
 // Dense and sparse decode attention over a paged KV cache (split partials + combine).
 //
-// TensorFold PR #1169 "What this changes": fn_attn_chunks reads its key and value
-// tiles through pg_at, looking a key's row up once per tile (key_at in shared
-// memory, beside key_ids).  PR #1170 commit ce5b78d: the contiguous path branches
+// TensorFold PR #1169 "What this changes": fn_attn_chunks gets its key and value
+// tiles via pg_at, resolving each key's row a single time per tile and keeping the
+// result (key_at) in shared memory next to key_ids.  PR #1170 commit ce5b78d: the contiguous path branches
 // once instead of testing the table for every key.  Here the only table test is
 // inside pg_at, taken once per key per tile while key_at is staged in LDS.
 //
@@ -24,9 +24,8 @@
 // combine kernel.  No atomics anywhere.
 //
 // Element types: float32 and bf16 rows (q of the same type), and e4m3 rows with
-// one float32 scale a row (TensorFold PR #1170, commit 5c09685 "--kv-cache fp8
-// through the page table too": a row's e4m3 codes and fp32 scale, the row's page
-// from the table).  For e4m3 the q rows are bf16; codes widen to bf16 exactly, so
+// one float32 scale a row (TensorFold PR #1170, commit 5c09685: in fp8 mode each
+// row's codes and its float32 scale are found via the row's page in the table).  For e4m3 the q rows are bf16; codes widen to bf16 exactly, so
 // a score is zscale * k_scale * (q . codes) and a probability enters PV as
 // p * v_scale (the softmax sum keeps p).  The scales of a tile's keys are read
 // through the same page lookup as its rows and staged in LDS beside key_at.

@@ -1,8 +1,8 @@
 // Decode attention on the matrix cores, for bf16 rows and e4m3 rows (bf16 queries), and for a
 // window of several queries a stream.
 //
-// TensorFold PR #1169 "What this changes": fn_attn_chunks reads its key and value tiles through
-// pg_at, one lookup per key per tile (key_at beside key_ids); PR #1170 commit ce5b78d: attention
+// TensorFold PR #1169 "What this changes": fn_attn_chunks gets its key and value tiles via pg_at,
+// resolving each key's row a single time per tile (key_at kept next to key_ids); PR #1170 commit ce5b78d: attention
 // partials merged afterwards; commit 5c09685: e4m3 rows with a float32 scale a row through the
 // table.  The name fn_attn_chunks_ahead (PR #1169) is taken as the windowed form: W query tokens at
 // the end of the cache, query w at position n - W + w seeing keys 0 .. n - W + w.

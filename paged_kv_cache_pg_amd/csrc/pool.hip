@@ -1,11 +1,11 @@
 // Host page pool for a KV arena: hands out pages for the page tables and runs of consecutive
 // pages, in the caller's memory (no allocation, no global state).
 //
-// TensorFold PR #1170, commit 1ac2075 ("a pool lane's recurrent state is a run of pool pages"):
-// the free stack hands out KV pages from the bottom; findRun / claimRun / releaseRun take k
-// consecutive free pages from the top; a pool too fragmented for a run makes the request wait.
-// Description of PR #1170: a lane's pages and run go back once the engine's stream drains (the
-// caller's duty: nothing here touches the GPU).
+// TensorFold PR #1170, commit 1ac2075 (a pool lane keeps its recurrent state in a run of pool
+// pages): single KV pages come off a free stack from the low end of the arena; findRun /
+// claimRun / releaseRun take k adjacent free pages from the high end; with no such run free, the
+// request waits.  Description of PR #1170: pages and runs are returned only after the engine's
+// stream has drained (the caller's duty: nothing here touches the GPU).
 //
 // State (host memory the caller owns, paged_pool_state_bytes(n) bytes):
 //   header | below[n] int32 | above[n] int32 | kind[n] uint8

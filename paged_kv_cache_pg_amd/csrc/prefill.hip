@@ -1,7 +1,7 @@
 // Chunked causal prefill over a paged KV cache on MFMA (bf16 in, fp32 accumulate).
 //
 // TensorFold PR #1170 (maintainer reply): prompt batches that read paged caches take a
-// "page-run path" while flat ones use tensor-core attention; the page-run path had lost
+// page-run path while flat ones use tensor-core attention; the page-run path had lost
 // prompt speed until tensor-core attention came back.  Here one MFMA kernel serves both
 // forms: the only difference is pg_at, taken once per key per tile while the tile's key
 // offsets are staged in LDS.

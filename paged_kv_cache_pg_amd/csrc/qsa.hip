@@ -1,7 +1,7 @@
 // Block pooling, block scores and top-k block selection over a paged cache.
 //
-// TensorFold PR #1169 "What this changes": a page of n positions holds the
-// indexer keys of its n positions and the pooled rows of their n/4 blocks;
+// TensorFold PR #1169 "What this changes": besides keys and values, each page of
+// n positions stores their indexer keys and one pooled row for each n/4 block;
 // fn_qsa_pool reads and writes through pg_at once per block of four, and
 // fn_qsa_scores reads the pooled rows through pg_at.  The selection itself is
 // not described on the pages; it keeps the k highest scores with the lower

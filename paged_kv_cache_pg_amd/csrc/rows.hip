@@ -1,8 +1,8 @@
 // Row stores and gathers through the page table, and the addressing test hook.
 //
-// TensorFold PR #1169 "What this changes": fn_attn_prep stores keys, values and
-// indexer keys through pg_at, and prompt-cache saves and restores copy page runs
-// in the contiguous layout so kept states move between the two forms.
+// TensorFold PR #1169 "What this changes": fn_attn_prep writes keys, values and
+// indexer keys at pg_at addresses, and saving or restoring a prompt cache moves runs
+// of pages to and from the contiguous layout, so a kept state passes between the forms.
 #include "internal.h"
 
 namespace paged {

@@ -1,15 +1,15 @@
 """Arena layout of one attention layer inside a page (the library side's own description).
 
-TensorFold PR #1169 "What this changes": a page of n positions holds, for each
-attention layer, the keys, values and indexer keys of its n positions and the
-pooled rows of their n/4 blocks; a cache pointer is its layer's part of page 0.
+TensorFold PR #1169 "What this changes": each page covers n positions and stores,
+per attention layer, their keys, values and indexer keys plus one pooled row for
+each of their n/4 blocks; each cache pointer addresses its layer's share of page 0.
 PR #1170 commit 3f5b87d gives the in-page order [key, value][head][position][row].
 This package lays a page out as
 
     K [Hkv][n][D] | V [Hkv][n][D] | IK [n][DI] | POOL [n/4][DI] float32
 
 and hands the kernels one base pointer per region.  e4m3 pages (PR #1170 commit
-5c09685: a row's e4m3 codes and fp32 scale; the page size in bytes) hold
+5c09685: fp8 rows keep e4m3 codes plus a float32 scale, and page sizes count bytes) hold
 
     K codes [Hkv][n][D] | V codes [Hkv][n][D] | K scales [Hkv][n] float32 | V scales [Hkv][n] float32
 

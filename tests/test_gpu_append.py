@@ -1,7 +1,8 @@
 """GPU parity of paged_kv_append: a step's K, V and indexer-key rows stored through the table and
 the pooled rows of the blocks the step completes, against the oracle's placement and pooling.
 
-TensorFold PR #1169 "Receipt": the stores and the pooled rows equal contiguous; guards intact.
+TensorFold PR #1169 "Receipt": stored rows and pooled rows match the contiguous layout, and the
+guards are left untouched.
 Bar: the arena after a sequence of appends equals, byte for byte, the oracle's arena (rows placed
 through its own row addressing, pooled rows from its own float64 pooling).
 """

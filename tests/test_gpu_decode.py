@@ -1,9 +1,10 @@
 """GPU parity of dense decode (paged_attn_decode) with the float64 oracle.
 
-Bar (TensorFold PR #1169 "Receipt"): paged output equals contiguous bit for bit
-over three repeats, attention rows stay within a float64 bound (here 2e-3
-max-norm relative per row), guards and inputs stay intact, and the two red
-controls (a swapped table over placed pages, a planted row) fail.
+Bar (TensorFold PR #1169 "Receipt"): paged and contiguous outputs agree bit for bit
+on each of three runs, every attention row is within the float64 bound (here 2e-3
+max-norm relative per row), guards and inputs are left untouched, and both red
+controls (pages placed under one table but read through another; one placed row
+overwritten) are caught.
 """
 import numpy as np
 import pytest
@@ -84,7 +85,8 @@ def test_mixed_pair_concurrent_equals_solo():
 
 
 def test_red_controls():
-    """A swapped table over placed pages and a planted row must both change the output."""
+    """Reading placed pages through a different table, and overwriting one placed row, must each
+    change the output."""
     w = make_workload(3, [600, 600], 16, 16, 4, dtype="bf16", table_kind="shuffled")
     pl = Placed(w)
     q = dev(w.q)

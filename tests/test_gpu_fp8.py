@@ -1,8 +1,8 @@
 """GPU parity of the e4m3 path: rows of e4m3 codes with a float32 scale a row, read through the
 page table (TensorFold PR #1170 commit 5c09685).
 
-Bar (the same commit: the fp8 reference dequantizes e4m3 x scale in float64; paged == contiguous
-in every shape): decode and sparse attention within 2e-3 (max-norm relative per row) of the
+Bar (the same commit: the fp8 check takes code times scale in float64, and paged must equal
+contiguous for every shape): decode and sparse attention within 2e-3 (max-norm relative per row) of the
 float64 oracle over code x scale, paged output equal to contiguous bit for bit, and the e4m3 store
 writing exactly the oracle quantizer's codes and scales through the table.
 """

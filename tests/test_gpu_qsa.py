@@ -1,8 +1,8 @@
 """GPU parity of block pooling, block scores + top-k, sparse attention and row
 stores/gathers with the float64 oracle.
 
-TensorFold PR #1169 "Receipt": block scores, sparse attention rows, the stores
-and the pooled rows equal contiguous over three repeats.  Pooled rows, scores
+TensorFold PR #1169 "Receipt": for block scores, sparse attention rows, stores
+and pooled rows, paged results match contiguous on each of three runs.  Pooled rows, scores
 and top-k ids are compared bit for bit with the oracle (both sides use the same
 float64 order); sparse attention rows within 2e-3 (max-norm relative a row).
 """

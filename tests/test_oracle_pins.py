@@ -83,7 +83,8 @@ def test_paged_equals_contiguous_arena_bytes():
 
 
 def test_red_controls_swapped_table_and_planted_row():
-    """PR #1169 "Receipt": a swapped table over placed pages and a planted row must both fail."""
+    """PR #1169 "Receipt": pages read through another table than they were placed with, and one
+    overwritten row, must each be caught."""
     w = make_workload(11, [40, 24], 8, 4, 2, head_dim=8, dtype="f32", table_kind="shuffled")
     lay = O.PageLayout(2, 8, 8, "f32")
     arena = O.place(lay, w.table, w.n_pages, w.lens, w.K, w.V)

@@ -2,9 +2,9 @@
 sequences, and the library's pool (through the C ABI) must agree with the model, page id for
 page id, over random sequences of requests.
 
-TensorFold PR #1170, commit 1ac2075: the free stack hands out KV pages from the bottom;
-runs of k consecutive free pages come from the top; a pool too fragmented for a run makes the
-request wait.
+TensorFold PR #1170, commit 1ac2075: single KV pages leave the free stack from the low end of
+the arena; runs of k adjacent free pages are taken from the high end; with no such run free,
+the request waits.
 """
 import numpy as np
 import pytest
