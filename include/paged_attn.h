@@ -332,7 +332,9 @@ int paged_row_offsets(const paged_pg *pg, int32_t n_streams, int32_t row_width,
  *   claim_run    the highest k consecutive free pages (*first = the lowest of them),
  *                taken off the free stack; PAGED_EFULL when no such run exists
  *   release_run  a claimed run's pages go back onto the stack, its lowest page on top;
- *                PAGED_EINVAL unless every page of [first, first+k) belongs to a run
+ *                PAGED_EINVAL, with nothing changed, unless (first, k) is a run exactly
+ *                as claim_run handed it out and not yet released (part of a run, or
+ *                two adjacent runs as one, is refused)
  *   free_count   pages on the free stack (negative status for a bad state)
  */
 size_t  paged_pool_state_bytes(int32_t n_pages);

@@ -11,7 +11,8 @@ Readings where the pages are silent:
     1, 2, ... (the bottom of the arena first);
   * a run is the highest k consecutive free pages; its pages leave the free stack
     (the others keep their order) and come back onto it with the run's lowest page
-    on top;
+    on top; only a run exactly as it was claimed can be released (not part of one,
+    not two together, not twice);
   * freed pages go back onto the stack in list order, the last listed on top;
   * a request that cannot be met takes nothing ("waits"); freeing a page that was
     not handed out, or listing one twice, is refused and changes nothing.
@@ -31,6 +32,7 @@ class PagePool:
         self.n = n_pages
         self.stack: List[int] = list(range(n_pages - 1, -1, -1))  # top = last element = page 0
         self.kind = [FREE] * n_pages
+        self.runs = {}  # lowest page of each claimed run -> its length
 
     def free_count(self) -> int:
         return len(self.stack)
@@ -60,13 +62,15 @@ class PagePool:
             if all(self.kind[p] == FREE for p in range(first, first + k)):
                 for p in range(first, first + k):
                     self.kind[p] = RUN
+                self.runs[first] = k
                 self.stack = [p for p in self.stack if self.kind[p] == FREE]
                 return first
         return None
 
     def release_run(self, first: int, k: int) -> bool:
-        if first < 0 or first + k > self.n or any(self.kind[p] != RUN for p in range(first, first + k)):
+        if self.runs.get(first) != k:
             return False
+        del self.runs[first]
         for p in range(first + k - 1, first - 1, -1):
             self.kind[p] = FREE
             self.stack.append(p)

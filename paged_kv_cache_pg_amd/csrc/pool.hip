@@ -31,7 +31,9 @@ struct PoolHeader {
   int32_t reserved;
 };
 
-enum : uint8_t { KIND_FREE = 0, KIND_PAGE = 1, KIND_RUN = 2, KIND_MARK = 3 };
+// A claimed run's lowest page is KIND_RUN and keeps the run's length in its stack link (below[],
+// unused while the page is off the stack); its other pages are KIND_RUN_BODY.
+enum : uint8_t { KIND_FREE = 0, KIND_PAGE = 1, KIND_RUN = 2, KIND_MARK = 3, KIND_RUN_BODY = 4 };
 
 size_t state_bytes(int64_t n) {
   const size_t b = sizeof(PoolHeader) + (size_t)n * 2 * sizeof(int32_t) + (size_t)n;
@@ -158,8 +160,9 @@ int paged_pool_claim_run(void* state, int32_t k, int32_t* first) {
   // out of the free stack, the order of the rest kept
   for (int32_t p = found; p < found + k; ++p) {
     unlink(v, p);
-    v.kind[p] = KIND_RUN;
+    v.kind[p] = p == found ? KIND_RUN : KIND_RUN_BODY;
   }
+  v.below[found] = k;
   *first = found;
   return PAGED_OK;
 }
@@ -167,8 +170,10 @@ int paged_pool_claim_run(void* state, int32_t k, int32_t* first) {
 int paged_pool_release_run(void* state, int32_t first, int32_t k) {
   View v;
   if (!view_of(state, &v) || k < 1 || first < 0 || (int64_t)first + k > v.h->n_pages) return PAGED_EINVAL;
-  for (int32_t p = first; p < first + k; ++p)
-    if (v.kind[p] != KIND_RUN) return PAGED_EINVAL;
+  // only a run exactly as claim_run handed it out: not part of one, not two together
+  if (v.kind[first] != KIND_RUN || v.below[first] != k) return PAGED_EINVAL;
+  for (int32_t p = first + 1; p < first + k; ++p)
+    if (v.kind[p] != KIND_RUN_BODY) return PAGED_EINVAL;
   // pushed from the top page down, so the run's lowest page comes off the stack first
   for (int32_t p = first + k - 1; p >= first; --p) push(v, p);
   return PAGED_OK;

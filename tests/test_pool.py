@@ -62,6 +62,18 @@ def test_model_release_puts_the_run_lowest_page_on_top():
     assert m.alloc(3) == [2, 3, 4]
 
 
+def test_model_release_takes_only_a_run_as_claimed():
+    m = PagePool(8)
+    assert m.claim_run(2) == 6 and m.claim_run(2) == 4
+    assert not m.release_run(6, 1)      # part of a run
+    assert not m.release_run(7, 1)      # part of a run, not its lowest page
+    assert not m.release_run(4, 4)      # two adjacent runs as one
+    assert m.free_count() == 4
+    assert m.release_run(4, 2)
+    assert not m.release_run(4, 2)      # released twice
+    assert m.release_run(6, 2) and m.free_count() == 8
+
+
 def test_model_refusals_change_nothing():
     m = PagePool(4)
     assert m.alloc(5) is None and m.free_count() == 4
@@ -103,6 +115,18 @@ def test_library_pool_refusals():
     with pytest.raises(P.PagedError):
         P.paged_pool_release_run(st, 0, 2)
     assert P.paged_pool_free_count(st) == 2
+    # only a run as claimed: not part of one, not two adjacent ones, not twice
+    st = _lib_pool(8)
+    assert P.paged_pool_claim_run(st, 2) == 6 and P.paged_pool_claim_run(st, 2) == 4
+    for first, k in ((6, 1), (7, 1), (4, 4), (5, 2)):
+        with pytest.raises(P.PagedError):
+            P.paged_pool_release_run(st, first, k)
+    assert P.paged_pool_free_count(st) == 4
+    P.paged_pool_release_run(st, 4, 2)
+    with pytest.raises(P.PagedError):
+        P.paged_pool_release_run(st, 4, 2)
+    P.paged_pool_release_run(st, 6, 2)
+    assert P.paged_pool_free_count(st) == 8
     bad = np.zeros(64, np.uint8)        # never initialised
     with pytest.raises(P.PagedError):
         P.paged_pool_free_count(bad)
@@ -116,7 +140,7 @@ def test_library_pool_matches_model_on_random_requests(seed, n):
     held_pages, held_runs = [], []
     buf = np.zeros(n, np.int32)
     for _ in range(600):
-        op = rng.integers(0, 4)
+        op = rng.integers(0, 5)
         if op == 0:
             k = int(rng.integers(0, max(2, n // 8)))
             want = m.alloc(k)
@@ -144,4 +168,11 @@ def test_library_pool_matches_model_on_random_requests(seed, n):
             first, k = held_runs.pop(int(rng.integers(0, len(held_runs))))
             assert m.release_run(first, k)
             P.paged_pool_release_run(st, first, k)
+        elif op == 4:
+            # a release of some range that is not a held run: both refuse and nothing changes
+            first, k = int(rng.integers(-2, n + 2)), int(rng.integers(1, 5))
+            if (first, k) not in held_runs:
+                assert not m.release_run(first, k)
+                with pytest.raises(P.PagedError):
+                    P.paged_pool_release_run(st, first, k)
         assert P.paged_pool_free_count(st) == m.free_count()
