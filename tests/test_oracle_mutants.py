@@ -1,0 +1,102 @@
+"""The oracle's pins catch plausible mistakes: each case plants one mistake in an oracle function
+(on the CPU, through a wrapper that swaps the module attribute the pins call) and requires that at
+least one of the pins written for that function then fails.  The unmodified oracle passes the same
+pins in tests/test_oracle_pins.py and tests/test_oracle_fp8.py."""
+import numpy as np
+import pytest
+
+import oracle as O
+import test_oracle_fp8 as F
+import test_oracle_pins as T
+
+_decode, _window, _prefill, _sparse = O.decode, O.decode_window, O.prefill, O.sparse
+_pool, _scores, _topk = O.pool, O.scores, O.topk
+_row_offset, _e4m3_value, _e4m3_encode = O.row_offset, O.e4m3_value, O.e4m3_encode
+
+
+def _head_modulo(q, K, V, lens, scale):
+    """Query head h reads KV head h mod Hkv instead of h // G."""
+    Hq, Hkv = q.shape[1], K.shape[1]
+    idx = [h % Hkv for h in range(Hq)]
+    return _decode(q, K[:, idx], V[:, idx], lens, scale)
+
+
+def _topk_ties_high(score, k):
+    order = sorted(range(len(score)), key=lambda b: (-score[b], -b))
+    return np.sort(np.array(order[:min(k, len(score))], dtype=np.int64))
+
+
+def _topk_score_order(score, k):
+    order = sorted(range(len(score)), key=lambda b: (-score[b], b))
+    return np.array(order[:min(k, len(score))], dtype=np.int64)
+
+
+def _e4m3_no_saturation(y):
+    y = np.asarray(y, dtype=np.float64)
+    c = np.asarray(_e4m3_encode(y)).copy()
+    big = np.abs(y) > 448
+    c[big] = np.where(y[big] < 0, 0xFF, 0x7F)   # NaN codes instead of +-448
+    return c
+
+
+def _window_attends_whole_cache(q, K, V, lens, scale):
+    S, W = q.shape[:2]
+    return np.stack([_decode(q[:, w], K, V, lens, scale) for w in range(W)], axis=1)
+
+
+BRUTE = [lambda: T.test_decode_matches_50_digit_brute_force(4, 5, 2),
+         lambda: T.test_decode_matches_50_digit_brute_force(8, 12, 4)]
+DECODE_PINS = [T.test_decode_single_key_is_value_row, T.test_decode_zero_query_is_mean_of_values_over_exactly_L_rows,
+               T.test_decode_two_keys_logistic_closed_form, T.test_decode_gqa_head_map_is_division,
+               T.test_decode_dominant_key_and_affine_equivariance, T.test_decode_empty_stream_is_zero, *BRUTE]
+
+MUTANTS = {
+    "decode drops the scale": ("decode", lambda q, K, V, lens, scale: _decode(q, K, V, lens, 1.0), DECODE_PINS),
+    "decode doubles the scale": ("decode", lambda q, K, V, lens, scale: _decode(q, K, V, lens, 2 * scale), DECODE_PINS),
+    "decode reads one key too few": ("decode", lambda q, K, V, lens, scale:
+                                     _decode(q, K, V, [max(int(l) - 1, 0) for l in lens], scale), DECODE_PINS),
+    "decode maps heads modulo": ("decode", _head_modulo, DECODE_PINS),
+    "decode swaps keys and values": ("decode", lambda q, K, V, lens, scale: _decode(q, V, K, lens, scale), DECODE_PINS),
+    "prefill drops the causal mask": ("prefill", lambda q, K, V, q_pos0, scale, causal=True, rows=None:
+                                      _prefill(q, K, V, q_pos0, scale, False, rows),
+                                      [T.test_prefill_first_row_and_causal_mask_offsets,
+                                       T.test_prefill_rows_equal_decode_and_chunking_invariance]),
+    "window queries see the whole cache": ("decode_window", _window_attends_whole_cache,
+                                           [T.test_decode_window_closed_form_and_short_streams,
+                                            T.test_decode_window_equals_causal_prefill_and_decode,
+                                            T.test_decode_window_matches_50_digit_brute_force]),
+    "sparse ignores the block ids": ("sparse", lambda q, K, V, ids, scale:
+                                     _decode(q, K, V, [K.shape[2]] * q.shape[0], scale),
+                                     [T.test_sparse_all_blocks_is_dense_and_subset_is_row_restriction]),
+    "pool divides by 3": ("pool", lambda IK, lens: [None if x is None else np.float32(x * (4 / 3))
+                                                    for x in _pool(IK, lens)],
+                          [T.test_pool_closed_forms, T.test_pool_of_short_stream_is_empty]),
+    "scores sum the dims backwards": ("scores", lambda qI, pooled:
+                                      _scores(np.ascontiguousarray(qI[:, ::-1]), np.ascontiguousarray(pooled[:, ::-1])),
+                                      [T.test_scores_exact_on_integers_and_linear_in_heads,
+                                       T.test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim]),
+    "scores sum the heads first": ("scores", lambda qI, pooled: _scores(qI.sum(axis=0, keepdims=True), pooled),
+                                   [T.test_scores_exact_on_integers_and_linear_in_heads,
+                                    T.test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim]),
+    "top-k ties go to the higher id": ("topk", _topk_ties_high, [T.test_topk_matches_python_sort_and_ties]),
+    "top-k ids in score order": ("topk", _topk_score_order, [T.test_topk_matches_python_sort_and_ties]),
+    "row offset one row off": ("row_offset", lambda *a, **k: _row_offset(*a, **k) + a[6],
+                               [T.test_row_offset_hand_derived]),
+    "e4m3 exponent bias 8": ("e4m3_value", lambda c: np.asarray(_e4m3_value(c)) * 0.5,
+                             [F.test_e4m3_values_derived_by_hand, F.test_e4m3_values_match_torch_float8_e4m3fn]),
+    "e4m3 encode does not saturate": ("e4m3_encode", _e4m3_no_saturation,
+                                      [F.test_e4m3_encode_ties_go_to_the_even_code_and_large_values_saturate]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_a_planted_mistake_fails_a_pin(name, monkeypatch):
+    attr, mutant, pins = MUTANTS[name]
+    monkeypatch.setattr(O, attr, mutant)
+    failed = []
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:  # only a pin's own check counts; any other error is a broken case
+            failed.append(getattr(pin, "__name__", "pin"))
+    assert failed, f"no pin caught: {name}"
