@@ -12,6 +12,27 @@ import test_oracle_pins as T
 _decode, _window, _prefill, _sparse = O.decode, O.decode_window, O.prefill, O.sparse
 _pool, _scores, _topk = O.pool, O.scores, O.topk
 _row_offset, _e4m3_value, _e4m3_encode = O.row_offset, O.e4m3_value, O.e4m3_encode
+_pool_row_offset, _place, _gather, _quantize = O.pool_row_offset, O.place, O.gather, O.e4m3_quantize_rows
+
+
+def _gather_swapped(*a, **k):
+    K, V, IK = _gather(*a, **k)
+    return V, K, IK
+
+
+def _quantize_447(x):
+    """Row scale amax / 447 instead of amax / 448."""
+    codes, scales = _quantize(x)
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, (amax / np.float32(447)).astype(np.float32), np.float32(0))
+    div = np.where(amax > 0, scale, np.float32(1))[..., None]
+    return np.asarray(_e4m3_encode((x / div).astype(np.float32))).astype(np.uint8), scale.astype(np.float32)
+
+
+def _window_one_back(q, K, V, lens, scale):
+    """Window query w stands one position early (sees keys 0 .. L - W + w - 1)."""
+    return _window(q, K, V, [max(int(l) - 1, 0) for l in lens], scale)
 
 
 def _head_modulo(q, K, V, lens, scale):
@@ -84,6 +105,21 @@ MUTANTS = {
                                [T.test_row_offset_hand_derived]),
     "e4m3 exponent bias 8": ("e4m3_value", lambda c: np.asarray(_e4m3_value(c)) * 0.5,
                              [F.test_e4m3_values_derived_by_hand, F.test_e4m3_values_match_torch_float8_e4m3fn]),
+    "pooled-row offset one row off": ("pool_row_offset", lambda *a, **k: _pool_row_offset(*a, **k) + a[5],
+                                      [T.test_pool_row_offset_hand_derived]),
+    "place swaps keys and values": ("place", lambda lay, table, n, lens, K, V, IK=None:
+                                    _place(lay, table, n, lens, V, K, IK),
+                                    [lambda: T.test_place_gather_round_trip("shuffled", 12),
+                                     lambda: T.test_place_gather_round_trip("reversed", 4)]),
+    "gather swaps keys and values": ("gather", _gather_swapped,
+                                     [lambda: T.test_place_gather_round_trip("shuffled", 12),
+                                      lambda: T.test_place_gather_round_trip("identity", 16)]),
+    "window queries one position early": ("decode_window", _window_one_back,
+                                          [T.test_decode_window_closed_form_and_short_streams,
+                                           T.test_decode_window_equals_causal_prefill_and_decode,
+                                           T.test_decode_window_matches_50_digit_brute_force]),
+    "e4m3 row scale amax / 447": ("e4m3_quantize_rows", _quantize_447,
+                                  [F.test_quantize_rows_invariants, F.test_quantize_rows_special_rows]),
     "e4m3 encode does not saturate": ("e4m3_encode", _e4m3_no_saturation,
                                       [F.test_e4m3_encode_ties_go_to_the_even_code_and_large_values_saturate]),
 }
