@@ -13,10 +13,6 @@ namespace {
 
 constexpr int64_t MAX_POS = (int64_t)1 << 30;
 
-#ifndef PAGED_DECODE_MFMA_BF16
-#define PAGED_DECODE_MFMA_BF16 0  // one-query decode of bf16 rows on the MFMA kernel
-#endif
-
 inline bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline int esize(int32_t dt) { return dt == PAGED_FP8_E4M3 ? 1 : dt == PAGED_BF16 ? 2 : 4; }
 // types of q, indexer keys, pooled and copied rows
@@ -134,11 +130,9 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq,
   a.out = out;
   const int elem = fp8 ? 2 : kv->dtype == PAGED_BF16 ? 1 : 0;
   const int G = n_q_heads / kv->n_kv_heads;
-  // bf16 and e4m3 rows take the MFMA decode; float32 rows the vector-ALU one
-  // Windows and e4m3 rows take the MFMA decode (e4m3 decode is ALU-bound on the vector units); one
-  // query over bf16 rows the vector-ALU decode, which measures faster there; float32 rows always the latter.
-  if (nq > 1 || fp8 || (elem == 1 && PAGED_DECODE_MFMA_BF16))
-    return hip_status(launch_decode_mfma(a, elem, G, n_streams, stream));
+  // Windows and e4m3 rows take the MFMA decode (e4m3 decode is bound by the vector units there); one
+  // query over bf16 or float32 rows takes the vector-ALU decode.
+  if (nq > 1 || fp8) return hip_status(launch_decode_mfma(a, elem, G, n_streams, stream));
   return hip_status(launch_decode(a, elem, G, n_streams, stream));
 }
 

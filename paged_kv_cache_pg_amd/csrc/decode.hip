@@ -23,12 +23,8 @@
 // Waves merge in order inside the workgroup, splits merge in order in the
 // combine kernel.  No atomics anywhere.
 //
-// Element types: float32 and bf16 rows (q of the same type), and e4m3 rows with
-// one float32 scale a row (TensorFold PR #1170, commit 5c09685: in fp8 mode each
-// row's codes and its float32 scale are found via the row's page in the table).  For e4m3 the q rows are bf16; codes widen to bf16 exactly, so
-// a score is zscale * k_scale * (q . codes) and a probability enters PV as
-// p * v_scale (the softmax sum keeps p).  The scales of a tile's keys are read
-// through the same page lookup as its rows and staged in LDS beside key_at.
+// Element types: float32 and bf16 rows, with q of the same type.  (e4m3 rows take the
+// MFMA decode, decode_mfma.hip.)
 #include "split.h"
 
 namespace paged {
@@ -42,33 +38,18 @@ namespace {
 #ifndef PAGED_DEC_RING_SHORT
 #define PAGED_DEC_RING_SHORT 4   // the same for streams of at most two tiles a wave
 #endif
-#ifndef PAGED_DEC_RING_FP8
-#define PAGED_DEC_RING_FP8 4     // the same for e4m3 rows
-#endif
-#ifndef PAGED_DEC_RING_FP8_SHORT
-#define PAGED_DEC_RING_FP8_SHORT 4
-#endif
 #ifndef PAGED_DEC_WG_PER_CU
 #define PAGED_DEC_WG_PER_CU 1    // workgroups a CU the register budget is set for
 #endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <int ET> struct Rows {
-  static constexpr int ROWB = ET == ET_F32 ? HD * 4 : ET == ET_BF16 ? HD * 2 : HD;  // K/V row bytes
-  static constexpr int QROWB = ET == ET_F32 ? HD * 4 : HD * 2;                    // q row bytes
+  static_assert(ET == ET_F32 || ET == ET_BF16, "float32 or bf16 rows");
+  static constexpr int ROWB = ET == ET_F32 ? HD * 4 : HD * 2;  // K/V (and q) row bytes
+  static constexpr int QROWB = ROWB;
   static constexpr int NCQ = ROWB / 256;  // 16-byte K chunks a lane in QK (16 lanes a key)
   static constexpr int NQC = QROWB / 256; // 16-byte q chunks a lane and head
 };
-
-__device__ __forceinline__ uint2 ld_stream8(const char* p) {
-#if PAGED_DEC_NT
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
-  return make_uint2(v.x, v.y);
-#else
-  return *(const uint2*)p;
-#endif
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
@@ -163,81 +144,56 @@ __device__ __forceinline__ float head_sum8(float v) {
 }
 
 // Partial dot product of a lane's q chunks with its K chunks (16 lanes a key).
-//   f32:  4 chunks of 4 dims;  bf16: 2 chunks of 8 dims;  e4m3: one chunk of 16 codes against 16 bf16 q dims
-// (two q chunks), the codes widened to bf16 pairs exactly (every e4m3 value is a bf16 value).
+//   f32:  4 chunks of 4 dims;  bf16: 2 chunks of 8 dims.
 template <int ET>
 __device__ __forceinline__ float qk_dot(const uint4 (&q)[Rows<ET>::NQC], const uint4 (&k)[Rows<ET>::NCQ]) {
   float acc = 0.f;
-  if constexpr (ET == ET_FP8) {
-    const uint32_t kw[4] = {k[0].x, k[0].y, k[0].z, k[0].w};
-    const uint32_t qw[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bf16x2_t k01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[c], 1.0f, false);
-      const bf16x2_t k23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[c], 1.0f, true);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[2 * c]), k01, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[2 * c + 1]), k23, acc, false);
-    }
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < Rows<ET>::NCQ; ++cc) {
-      if constexpr (ET == ET_BF16) {
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].x), __builtin_bit_cast(bf16x2_t, k[cc].x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].y), __builtin_bit_cast(bf16x2_t, k[cc].y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].z), __builtin_bit_cast(bf16x2_t, k[cc].z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].w), __builtin_bit_cast(bf16x2_t, k[cc].w), acc, false);
-      } else {
-        acc = fmaf(__uint_as_float(q[cc].x), __uint_as_float(k[cc].x), acc);
-        acc = fmaf(__uint_as_float(q[cc].y), __uint_as_float(k[cc].y), acc);
-        acc = fmaf(__uint_as_float(q[cc].z), __uint_as_float(k[cc].z), acc);
-        acc = fmaf(__uint_as_float(q[cc].w), __uint_as_float(k[cc].w), acc);
-      }
+  for (int cc = 0; cc < Rows<ET>::NCQ; ++cc) {
+    if constexpr (ET == ET_BF16) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].x), __builtin_bit_cast(bf16x2_t, k[cc].x), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].y), __builtin_bit_cast(bf16x2_t, k[cc].y), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].z), __builtin_bit_cast(bf16x2_t, k[cc].z), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[cc].w), __builtin_bit_cast(bf16x2_t, k[cc].w), acc, false);
+    } else {
+      acc = fmaf(__uint_as_float(q[cc].x), __uint_as_float(k[cc].x), acc);
+      acc = fmaf(__uint_as_float(q[cc].y), __uint_as_float(k[cc].y), acc);
+      acc = fmaf(__uint_as_float(q[cc].z), __uint_as_float(k[cc].z), acc);
+      acc = fmaf(__uint_as_float(q[cc].w), __uint_as_float(k[cc].w), acc);
     }
   }
   return acc;
 }
 
-// The 8 values a lane takes of one V row in PV (32 lanes a key; dims 8*j32 .. 8*j32+7 for bf16 and e4m3,
+// The 8 values a lane takes of one V row in PV (32 lanes a key; dims 8*j32 .. 8*j32+7 for bf16,
 // dims 4*j32 + {0..3, 128..131} for float32).  v holds the lane's chunks of the row in load order.
 template <int ET>
 __device__ __forceinline__ void pv_unpack(const uint4& v0, const uint4& v1, float* f) {
   if constexpr (ET == ET_BF16) {
     f[0] = bf16lo(v0.x); f[1] = bf16hi(v0.x); f[2] = bf16lo(v0.y); f[3] = bf16hi(v0.y);
     f[4] = bf16lo(v0.z); f[5] = bf16hi(v0.z); f[6] = bf16lo(v0.w); f[7] = bf16hi(v0.w);
-  } else if constexpr (ET == ET_F32) {
+  } else {
     f[0] = __uint_as_float(v0.x); f[1] = __uint_as_float(v0.y); f[2] = __uint_as_float(v0.z); f[3] = __uint_as_float(v0.w);
     f[4] = __uint_as_float(v1.x); f[5] = __uint_as_float(v1.y); f[6] = __uint_as_float(v1.z); f[7] = __uint_as_float(v1.w);
-  } else {
-    // e4m3: codes in v0.x (dims 0..3) and v0.y (dims 4..7), widened exactly to float32
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v0.x, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(v0.x, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(v0.y, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(v0.y, true);
-    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
   }
 }
 
 // One 4-key step of loads, the same register footprint for both kinds: a K step (QK, 16 lanes a
 // key) fills x[0 .. NCQ-1]; a V step (PV, 32 lanes a key, two half steps of 2 keys) fills half step j's
-// part of x (chunks NCP*j .. NCP*j+NCP-1, or for e4m3 the 8 bytes x[0] words 2j, 2j+1).  For e4m3, ok
-// bit j says that the key of V half step j is real: a masked key's stand-in bytes may hold NaN codes,
-// so its codes are replaced by zeros before they meet its zero probability.
+// part of x (chunks NCP*j .. NCP*j+NCP-1).
 template <int ET>
 struct StepBuf {
   uint4 x[Rows<ET>::NCQ];
-  uint32_t ok;
 };
 
 template <int ET, int G, int RING>
 __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(DecArgs a) {
   using RT = Rows<ET>;
-  constexpr bool FP8 = ET == ET_FP8;
   constexpr int ROWB = RT::ROWB;     // bytes a K/V row
   constexpr int QROWB = RT::QROWB;   // bytes a q row
   constexpr int NCQ = RT::NCQ;       // 16-byte K chunks a lane in QK
   constexpr int NQC = RT::NQC;       // 16-byte q chunks a lane and head
-  constexpr int NCP = FP8 ? 1 : ROWB / 512;  // V chunks a lane in PV (e4m3: one 8-byte piece)
+  constexpr int NCP = ROWB / 512;    // V chunks a lane in PV
   constexpr int NO = 8;              // outputs a lane a head
   constexpr int NSTEP = TILE / 4;    // 4-key steps a tile and phase
   constexpr int SPT = 2 * NSTEP;     // load steps a tile: NSTEP of K, then NSTEP of V
@@ -251,9 +207,6 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   __shared__ float s_o[NWAVE][G][HD];
   __shared__ float s_m[NWAVE][G];
   __shared__ float s_l[NWAVE][G];
-  // e4m3 row scales of the keys of the current and the next tile (K, V)
-  __shared__ float s_ks[FP8 ? NWAVE : 1][2][TILE];
-  __shared__ float s_vs[FP8 ? NWAVE : 1][2][TILE];
 
   // g: the group of G q heads g*G .. g*G+G-1; gk: their KV head (a KV head's q heads may be spread
   // over 2^kvshift groups)
@@ -309,34 +262,23 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
       for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream(kp + 256 * cc + 16 * jj);
     } else {
-      b.ok = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t off = s_keyat[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
-        const bool ok = ok_t && off >= 0;
-        const char* vp = ok ? a.vb + off : qrow;
-        if constexpr (FP8) {
-          const uint2 v = ld_stream8(vp + 8 * j32);
-          if (j == 0) { b.x[0].x = v.x; b.x[0].y = v.y; }
-          else        { b.x[0].z = v.x; b.x[0].w = v.y; }
-          b.ok |= ok ? (1u << j) : 0u;
-        } else {
+        const char* vp = (ok_t && off >= 0) ? a.vb + off : qrow;
 #pragma unroll
-          for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
-        }
+        for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
       }
     }
   };
 
-  // q rows of the G query heads of KV head g: the lane's 16 dims (f32 / bf16: chunks at 256*cc + 16*jj, the
-  // dims its K chunks hold; e4m3 rows: dims 16*jj .. 16*jj+15, bytes 32*jj .. 32*jj+31 of the bf16 row).
+  // q rows of the G query heads of KV head g: the lane's 16 dims, chunks at 256*cc + 16*jj (the dims
+  // its K chunks hold).
   uint4 qr[G][NQC];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int cc = 0; cc < NQC; ++cc)
-      qr[h][cc] = FP8 ? *(const uint4*)(qrow + h * QROWB + 32 * jj + 16 * cc)
-                      : *(const uint4*)(qrow + h * QROWB + 256 * cc + 16 * jj);
+    for (int cc = 0; cc < NQC; ++cc) qr[h][cc] = *(const uint4*)(qrow + h * QROWB + 256 * cc + 16 * jj);
 
   float m_run = NEG_INF, l_run = 0.f;  // for head lane % G
   float o[G][NO];
@@ -345,21 +287,11 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < NO; ++e) o[h][e] = 0.f;
 
-  // e4m3: the scales of a key, read through its page (the lookup its row takes); a masked key reads the
-  // region's first scale and gets V scale 0.
-  auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, gk, pos, 4) : 0; };
-
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
       const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
       s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
-      if constexpr (FP8) {
-        const int64_t so = scale_off(page0, pos0);
-        const float ks = *(const float*)(a.ksb + so), vs = *(const float*)(a.vsb + so);
-        s_ks[w][0][lane] = ks;
-        s_vs[w][0][lane] = pos0 >= 0 ? vs : 0.f;
-      }
     }
     int id_next = load_id(1);
     wave_lds_sync();
@@ -373,25 +305,12 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
       const int pos1 = key_pos(t + 1, id_next);
       const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
       id_next = load_id(t + 2);
-      float ks1 = 0.f, vs1 = 0.f;
 
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
         if (i == 4) {
           s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
-          if constexpr (FP8) {
-            const int64_t so = scale_off(page1, pos1);
-            ks1 = *(const float*)(a.ksb + so);
-            vs1 = *(const float*)(a.vsb + so);
-          }
           wave_lds_sync();
-        }
-        if constexpr (FP8) {
-          // tile t+1's scales, stored once their loads have long landed (read from tile t+1 on)
-          if (i == NSTEP + 4) {
-            s_ks[w][(t + 1) & 1][lane] = ks1;
-            s_vs[w][(t + 1) & 1][lane] = pos1 >= 0 ? vs1 : 0.f;
-          }
         }
         if (i == NSTEP) {
           // Online softmax over tile t.  Lane l takes head hh = l % G and the 8 keys 8k + m (k = 0..7,
@@ -414,8 +333,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float p = (ev[k] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(ev[k] - m_new);
-            // the PV weight of key 8k + m8 carries its V scale; the running sum does not
-            if (lane < 8 * G) sc[(8 * k + m8) * G + hh] = FP8 ? p * s_vs[w][t & 1][8 * k + m8] : p;
+            if (lane < 8 * G) sc[(8 * k + m8) * G + hh] = p;
             tsum += p;
           }
           tsum = head_sum8<G>(tsum);
@@ -448,10 +366,9 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
           const int kk = 4 * i + grp;
           if ((lane & 3) == 0 && R::writer_row(row)) {
             const bool valid = s_keyat[w][t & 3][kk] >= 0;
-            const float zs = FP8 ? a.zscale * s_ks[w][t & 1][kk] : a.zscale;
 #pragma unroll
             for (int k = 0; k < R::NR; ++k)
-              s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * zs : NEG_INF;
+              s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
           }
         } else {
           const float* pp = s_sc[w];
@@ -459,15 +376,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
           for (int j = 0; j < 2; ++j) {
             const int kk = 4 * (i - NSTEP) + 2 * j + half;
             float vf[NO];
-            if constexpr (FP8) {
-              const bool ok = (cur.ok >> j) & 1u;
-              uint4 v = {0u, 0u, 0u, 0u};
-              v.x = ok ? (j == 0 ? cur.x[0].x : cur.x[0].z) : 0u;
-              v.y = ok ? (j == 0 ? cur.x[0].y : cur.x[0].w) : 0u;
-              pv_unpack<ET>(v, v, vf);
-            } else {
-              pv_unpack<ET>(cur.x[NCP * j], cur.x[NCP * j + NCP - 1], vf);
-            }
+            pv_unpack<ET>(cur.x[NCP * j], cur.x[NCP * j + NCP - 1], vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               const float p = pp[kk * G + h];
@@ -493,7 +402,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < NO; ++e) {
-        // f32: dims 4*j32 + {0..3} and 128 + 4*j32 + {0..3}; bf16 / e4m3: dims 8*j32 + e
+        // f32: dims 4*j32 + {0..3} and 128 + 4*j32 + {0..3}; bf16: dims 8*j32 + e
         const int d = ET == ET_F32 ? (e < 4 ? 4 * j32 + e : 128 + 4 * j32 + e - 4) : 8 * j32 + e;
         s_o[w][h][d] = o[h][e];
       }
@@ -584,9 +493,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 
 // Ring depth: one step ahead keeps the register file small for long streams, where every wave has
 // several tiles and two waves share a SIMD; streams of at most two tiles a wave (short or sparse
-// key lists) run their few steps three ahead instead.  e4m3 steps carry half the bytes of bf16
-// steps, so they keep more steps in flight.  The depth changes only when loads are issued, never
-// the arithmetic, so results do not depend on it.
+// key lists) run their few steps three ahead instead.  The depth changes only when loads are
+// issued, never the arithmetic, so results do not depend on it.
 template <int ET, int G>
 hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
@@ -597,11 +505,6 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
       hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_SHORT>), grid, dim3(WGS), 0, st, a);
     else
       hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
-  } else if constexpr (ET == ET_FP8) {
-    if (short_keys)
-      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_FP8_SHORT>), grid, dim3(WGS), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_FP8>), grid, dim3(WGS), 0, st, a);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<ET, G, 2>), grid, dim3(WGS), 0, st, a);
   }
@@ -613,12 +516,14 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
 // Short key lists (at most two tiles a wave) leave most of the GPU idle and each wave waiting on its
 // own loads: there a KV head's q heads are spread over up to 2^PAGED_DEC_HSPLIT workgroups, which read
 // the same K/V rows (the second read mostly from L2), so twice the waves keep loads in flight, each
-// with fewer registers.
+// with fewer registers.  float32 rows hold twice the q registers of bf16 rows, so a float32 workgroup
+// takes at most 4 heads (8 would spill): a group of 8 always runs as two workgroups of 4.
 #ifndef PAGED_DEC_HSPLIT
 #define PAGED_DEC_HSPLIT 2
 #endif
 template <int ET>
 hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
+  constexpr int GMAX = ET == ET_F32 ? 4 : 8;  // heads a workgroup at most
   DecArgs a = a0;
   const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
   const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
@@ -626,11 +531,12 @@ hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
   if (short_keys) {
     while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1) ++a.kvshift;
   }
+  while ((G >> a.kvshift) > GMAX) ++a.kvshift;
   switch (G >> a.kvshift) {
     case 1: return launch_t<ET, 1>(a, n_streams, st);
     case 2: return launch_t<ET, 2>(a, n_streams, st);
     case 4: return launch_t<ET, 4>(a, n_streams, st);
-    case 8: return launch_t<ET, 8>(a, n_streams, st);
+    case 8: if constexpr (GMAX >= 8) return launch_t<ET, 8>(a, n_streams, st); break;
   }
   return hipErrorInvalidValue;
 }
@@ -654,7 +560,6 @@ hipError_t launch_decode(const DecArgs& a, int elem, int G, int n_streams, hipSt
   switch (elem) {
     case ET_F32: return launch_g<ET_F32>(a, G, n_streams, st);
     case ET_BF16: return launch_g<ET_BF16>(a, G, n_streams, st);
-    case ET_FP8: return launch_g<ET_FP8>(a, G, n_streams, st);
   }
   return hipErrorInvalidValue;
 }

@@ -375,11 +375,12 @@ hipError_t launch_w(const DecArgs& a, int n_streams, hipStream_t st) {
   return launch_decode_combine(a, n_streams, st);
 }
 
-// Windows of 1 to 4 queries, as long as window x group fits the 16 columns.
+// Windows of 2 to 4 queries, as long as window x group fits the 16 columns; one query only over e4m3
+// rows (one query over bf16 rows takes the vector-ALU decode).
 template <int ET, int G>
 hipError_t launch_g(const DecArgs& a, int n_streams, hipStream_t st) {
   switch (a.nq) {
-    case 1: return launch_w<ET, G, 1>(a, n_streams, st);
+    case 1: if constexpr (ET == ET_FP8) return launch_w<ET, G, 1>(a, n_streams, st); break;
     case 2: return launch_w<ET, G, 2>(a, n_streams, st);
     case 3: if constexpr (3 * G <= 16) return launch_w<ET, G, 3>(a, n_streams, st); break;
     case 4: if constexpr (4 * G <= 16) return launch_w<ET, G, 4>(a, n_streams, st); break;
