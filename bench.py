@@ -78,6 +78,20 @@ def _blas_threads() -> int:
         return 1
 
 
+def _affinity_cores() -> int:
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _oracle_threads() -> dict:
+    """What the host oracle ran on: the BLAS threads its matrix products used (the rest of it is one
+    Python thread) and the cores the process may use."""
+    return {"cores": _blas_threads(), "affinity_cores": _affinity_cores()}
+
+
 # ---------------------------------------------------------------------------
 # Batched paged decode (the headline)
 # ---------------------------------------------------------------------------
@@ -165,7 +179,7 @@ class DecodeBench:
             reps += 1
             del K, V
         kv_bytes = cls.S * cls.HKV * cls.L * cls.D * 2 * 2
-        return {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(),
+        return {"value": round(reps * kv_bytes / total / 1e9, 4), "unit": "GB/s", **_oracle_threads(),
                 "kind": "oracle",
                 "sample": f"whole decode workload (4 streams x 40960 positions, 32 q / 4 KV heads): gather through "
                           f"the table + float64 attention, {reps} passes in {total:.2f} s"}
@@ -218,6 +232,42 @@ class PrefillBench:
     def run(self, i: int = 0):
         for c0 in range(0, self.N, self.CHUNK):
             self.chunk(c0)
+
+    def oracle_rate(self, every: int = 4):
+        """The oracle's prompt throughput, from a bounded sample: every `every`-th query of the last two
+        chunks, all heads (those rows see almost the whole cache, so the oracle's work a row is the
+        algorithmic one), gathered through the table and attended in float64; the FLOP rate of the
+        sample is applied to the whole prompt's algorithmic FLOP."""
+        import numpy as np
+        import oracle as O
+        from paged_kv_cache_pg_amd.inputs import bf16_bits_to_f32
+        w = self.w
+        olay = O.PageLayout(self.HKV, self.D, self.PTOK, "bf16")
+        arena = O.place(olay, w.table, w.n_pages, w.lens, w.K, w.V)
+        flops, t_total, rows_done = 0.0, 0.0, 0
+        t0 = time.perf_counter()
+        K, V, _ = O.gather(olay, w.table, arena, w.lens)
+        Kf = bf16_bits_to_f32(K[0]).astype(np.float64)
+        Vf = bf16_bits_to_f32(V[0]).astype(np.float64)
+        t_total += time.perf_counter() - t0
+        del K, V, arena
+        for c0 in (self.N - 2 * self.CHUNK, self.N - self.CHUNK):
+            qc = np.ascontiguousarray(w.q[c0:c0 + self.CHUNK])
+            qf = bf16_bits_to_f32(qc).astype(np.float64)
+            rows = np.arange(0, self.CHUNK, every)
+            t0 = time.perf_counter()
+            O.prefill(qf, Kf, Vf, c0, 1 / 16, rows=rows)
+            t_total += time.perf_counter() - t0
+            flops += 4.0 * self.D * self.HQ * float(np.sum(c0 + rows + 1))
+            rows_done += len(rows)
+        rate = flops / t_total
+        tok_s = self.N / (self.flops / rate)
+        return {"value": round(tok_s, 2), "unit": "tokens/s", **_oracle_threads(), "kind": "oracle",
+                "sample": f"{rows_done} query rows x {self.HQ} heads of the {self.N}-token prompt (every {every}th "
+                          f"query of its last two chunks, {flops:.3e} of its {self.flops:.3e} algorithmic FLOP): "
+                          f"gather through the table + float64 attention in {t_total:.2f} s; the prompt's "
+                          f"tokens/s is that FLOP rate applied to the whole prompt",
+                "oracle_gflops": round(rate / 1e9, 2)}
 
     def check_last_chunk(self):
         import numpy as np
@@ -300,6 +350,36 @@ class SparseBench:
     def sparse(self, i=0):
         self.P.paged_sparse_attn(self.q, self.P.PAGED_BF16, self.HQ, self.kv, self.pg, self.ids, self.cnt, self.K,
                                  self.S, self.L, 1 / 16, self.out, self.sws)
+
+    def oracle_rate(self):
+        """The oracle over the whole block-sparse step of all three streams: indexer keys gathered
+        through the table and pooled, blocks scored, top-k selected, the selected K/V rows gathered
+        and attended, all in float64."""
+        import numpy as np
+        import oracle as O
+        from paged_kv_cache_pg_amd.inputs import bf16_bits_to_f32
+        w = self.w
+        olay = O.PageLayout(self.HKV, self.D, self.PTOK, "bf16", idx_dim=self.DI)
+        arena = O.place(olay, w.table, w.n_pages, w.lens, w.K, w.V, w.IK)
+        qf, qI = w.as_f64("q"), w.as_f64("qI")
+        t0 = time.perf_counter()
+        K, V, IK = O.gather(olay, w.table, arena, w.lens)
+        pooled = O.pool(bf16_bits_to_f32(IK).astype(np.float64), w.lens)
+        sel = [O.topk(O.scores(qI[s], pooled[s]), self.K) for s in range(self.S)]
+        Ks = np.zeros((self.S, self.HKV, 4 * self.K, self.D))
+        Vs = np.zeros_like(Ks)
+        for s in range(self.S):
+            pos = (4 * sel[s][:, None] + np.arange(4)[None, :]).reshape(-1)
+            Ks[s] = bf16_bits_to_f32(K[s][:, pos]).astype(np.float64)
+            Vs[s] = bf16_bits_to_f32(V[s][:, pos]).astype(np.float64)
+        O.decode(qf, Ks, Vs, [4 * self.K] * self.S, 1 / 16)
+        dt = time.perf_counter() - t0
+        nbytes = self.bytes_pool + self.bytes_scores + self.bytes_sparse
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "us": round(dt * 1e6, 1), **_oracle_threads(),
+                "kind": "oracle",
+                "sample": f"one whole block-sparse step of the 3 x 131072 workload (pooling, scores, top-{self.K}, "
+                          f"sparse attention; gathers through the table included) in {dt:.2f} s; GB/s of the "
+                          f"step's algorithmic bytes ({nbytes})"}
 
     def check(self):
         """Top-k ids of stream 0 against the oracle (bit for bit), one sparse row within 2e-3."""
@@ -645,8 +725,9 @@ def _sclk_now():
 class ClockSampler:
     """Samples the highest current shader clock sysfs reports every 20 ms on a background thread."""
 
-    def __init__(self):
+    def __init__(self, what: str = "decode steps"):
         import threading
+        self.what = what
         self.samples, self._stop = [], threading.Event()
         self._t = threading.Thread(target=self._run, daemon=True)
 
@@ -670,7 +751,7 @@ class ClockSampler:
             return None
         return {"median": statistics.median(self.samples), "min": min(self.samples), "max": max(self.samples),
                 "samples": len(self.samples),
-                "source": "sysfs pp_dpm_sclk current level, every 20 ms during the timed decode steps"}
+                "source": f"sysfs pp_dpm_sclk current level, every 20 ms during the timed {self.what}"}
 
 
 def run_page_pool():
@@ -753,25 +834,51 @@ def run_decode_fp8(args):
     return out
 
 
-def run_prefill(args):
+def time_runs(fn, runs: int, warmup: int = 1):
+    """Each of `runs` calls bracketed by its own pair of HIP events on the current stream (the
+    stream the library launches on); returns the per-run times in ms, sorted."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for i in range(runs):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def run_prefill(args, cpu_baseline: bool = False):
+    import statistics
     import torch
     prefill = {}
+    runs = max(5, args.steps // 4)
     for n_tok in (8192, 40960):
         pb = PrefillBench(n_tok)
-        ms, _ = time_steps(pb.run, max(1, args.steps // 10), 1)
+        with ClockSampler("prompt runs") as clk:
+            per = time_runs(pb.run, runs)
+        ms = statistics.median(per)
         perr = pb.check_last_chunk()
         tflops = pb.flops / (ms * 1e-3) / 1e12
         prefill[str(n_tok)] = {"tokens_per_s": round(n_tok / (ms * 1e-3), 1), "ms": round(ms, 3),
+                               "ms_min": round(per[0], 3), "ms_max": round(per[-1], 3), "runs": runs,
+                               "tokens_per_s_best": round(n_tok / (per[0] * 1e-3), 1),
                                "chunks": (n_tok + 2047) // 2048, "alg_tflops": round(tflops, 1),
-                               "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "oracle_max_rel_err": perr}
-        log(f"prefill {n_tok}: {ms:.2f} ms, {n_tok / (ms * 1e-3):.0f} tok/s, {tflops:.0f} TFLOP/s "
-            f"({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+                               "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "oracle_max_rel_err": perr,
+                               "gpu_sclk_mhz": clk.summary()}
+        log(f"prefill {n_tok}: median {ms:.2f} ms (min {per[0]:.2f}) over {runs} runs, {n_tok / (ms * 1e-3):.0f} "
+            f"tok/s, {tflops:.0f} TFLOP/s ({tflops / MFMA_BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        if cpu_baseline and n_tok == 40960:
+            prefill[str(n_tok)]["cpu_baseline"] = cb = pb.oracle_rate()
+            log(f"prefill {n_tok}: oracle {cb['value']:.1f} tokens/s ({cb['oracle_gflops']} GFLOP/s)")
         del pb
         torch.cuda.empty_cache()
     return prefill
 
 
-def run_sparse(args):
+def run_sparse(args, cpu_baseline: bool = False):
     sb = SparseBench()
     sparse = {}
     total_us = 0.0
@@ -802,6 +909,9 @@ def run_sparse(args):
     sparse["topk_ids_equal_oracle"] = ids_ok
     sparse["oracle_max_rel_err"] = serr
     log(f"sparse: scores + top-k + attention {total_us:.1f} us; ids == oracle: {ids_ok}; err {serr:.2e}")
+    if cpu_baseline:
+        sparse["cpu_baseline"] = cb = sb.oracle_rate()
+        log(f"sparse: oracle {cb['us'] / 1e6:.2f} s a step, {cb['value']} GB/s")
     del sb
     return sparse
 
@@ -845,17 +955,18 @@ def main():
     if args.only in (None, "decode_fp8"):
         result["decode_e4m3"] = run_decode_fp8(args)
         torch.cuda.empty_cache()
+    want_cpu = args.only is None and not args.no_cpu_baseline
     if args.only in (None, "prefill"):
-        result["prefill"] = run_prefill(args)
+        result["prefill"] = run_prefill(args, cpu_baseline=want_cpu)
         torch.cuda.empty_cache()
     if args.only in (None, "sparse"):
-        result["sparse"] = run_sparse(args)
+        result["sparse"] = run_sparse(args, cpu_baseline=want_cpu)
         torch.cuda.empty_cache()
     if args.only in (None, "append"):
         result["append"] = run_append(args)
         result["page_pool"] = run_page_pool()
         torch.cuda.empty_cache()
-    if args.only is None and not args.no_cpu_baseline:
+    if want_cpu:
         result["cpu_baseline"] = DecodeBench.cpu_baseline_from_scratch()
     print(json.dumps(result), flush=True)
 

@@ -302,11 +302,16 @@ int paged_kv_append(const void *k_new, const void *v_new, const void *ik_new, in
                     const int32_t *pos0, int32_t n_streams, int32_t max_len, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* Test hook: the row addressing itself, on the device.  out[i] = the element
- * offset of row (streams[i], heads[i], positions[i]) in a region whose page
- * part is [H][page_pos][row_width] -- the same device function every kernel
- * above uses.  Entries whose stream or position is negative or past the
- * table's extent get -1.
+/* Test hook: the row addressing itself, on the device.  [P1 "What this changes"]:
+ * pg_at gives, without a table, the earlier contiguous offset of a row and, with
+ * one, the base of the page holding the position plus the row's offset inside that
+ * page.  out[i] = that element offset of row (streams[i], heads[i], positions[i])
+ * in a region whose page part is [H][page_pos][row_width], from the same device
+ * function every kernel above uses; it lets a test compare the library's
+ * addressing with an independent one bit for bit.  Entries whose stream or
+ * position is negative or past the table's extent get -1.  Refusals as for every
+ * call (PAGED_EINVAL for a NULL pg, non-zero reserved, page_pos or page_elems
+ * below 1, a misaligned table, NULL arrays or a misaligned out).
  */
 int paged_row_offsets(const paged_pg *pg, int32_t n_streams, int32_t row_width,
                       const int32_t *streams, const int32_t *heads, const int32_t *positions,
@@ -345,7 +350,10 @@ int     paged_pool_claim_run(void *state, int32_t k, int32_t *first);
 int     paged_pool_release_run(void *state, int32_t first, int32_t k);
 int32_t paged_pool_free_count(const void *state);
 
-/* Text for a status code (static storage). */
+/* Text for a status code, so that a binding can raise an error that names the
+ * refusal (the pages' calls report why they refuse a page table: [P1 "Gotchas"],
+ * [P2 "What this changes"]).  Returns a pointer to static storage the caller must
+ * not free; an unknown code gives "unknown status". */
 const char *paged_strerror(int status);
 
 #ifdef __cplusplus

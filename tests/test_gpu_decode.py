@@ -145,9 +145,26 @@ def test_row_offsets_hook_bitwise():
     assert np.array_equal(got, want)
 
 
-def test_batched_decode_full_size_sampled():
-    """4 streams x 40960 positions, pages of 256 shuffled, 32 q / 4 KV heads, bf16: paged == contiguous
-    bit for bit; sampled rows against the oracle."""
+def _oracle_by_group(w, lens, scale=1 / 16):
+    """The oracle's rows for every (stream, q head), one (stream, KV head) at a time so that only one
+    group's rows are widened to float64 at once."""
+    S, Hq, Hkv = w.n_streams, w.n_q_heads, w.n_kv_heads
+    G = Hq // Hkv
+    qf = w.as_f64("q")
+    ref = np.zeros((S, Hq, w.head_dim))
+    for s in range(S):
+        for g in range(Hkv):
+            L = int(lens[s])
+            K = (w.K[s:s + 1, g:g + 1, :L].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            V = (w.V[s:s + 1, g:g + 1, :L].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            ref[s, g * G:(g + 1) * G] = O.decode(qf[s:s + 1, g * G:(g + 1) * G], K, V, [L], scale)[0]
+    return ref
+
+
+def test_batched_decode_full_size_every_row():
+    """4 streams x 40960 positions, pages of 256 shuffled, 32 q / 4 KV heads, bf16 (the launch the
+    benchmark times, five 64-key tiles a wave): paged == contiguous bit for bit, and every one of the
+    128 (stream, head) rows within the bound of the oracle."""
     w = make_workload(3, [40960] * 4, 256, 32, 4, dtype="bf16", table_kind="shuffled")
     pl = Placed(w)
     pc = Placed(w, paged=False)
@@ -155,11 +172,48 @@ def test_batched_decode_full_size_sampled():
     o1 = decode(pl, q, 1 / 16).cpu().numpy()
     o2 = decode(pc, q, 1 / 16).cpu().numpy()
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
-    qf, K, V = w.as_f64("q"), w.as_f64("K"), w.as_f64("V")
-    for s, h in [(0, 0), (1, 13), (2, 31), (3, 8)]:
-        ref = O.decode(qf[s:s + 1, h:h + 1], K[s:s + 1, h // 8:h // 8 + 1], V[s:s + 1, h // 8:h // 8 + 1],
-                       [40960], 1 / 16)
-        assert rel_err_rows(o1[s, h][None], ref[0]) <= TOL
+    del pl, pc
+    ref = _oracle_by_group(w, w.lens)
+    num = np.max(np.abs(o1 - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    assert np.all(num <= TOL * den), np.max(num / den)
+
+
+@pytest.mark.parametrize("ptok", [48, 256])
+def test_decode_four_and_more_tiles_a_wave_every_row(ptok):
+    """Streams long enough that each wave runs 3 to 5 tiles (its four-slot key_at ring wraps), G = 8:
+    lengths 40960, 32768, 24000 and 16500 over shuffled pages of 48 and 256: paged == contiguous bit
+    for bit, and every row within the bound of the oracle."""
+    lens = [40960, 32768, 24000, 16500]
+    w = make_workload(31, lens, ptok, 32, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    pc = Placed(w, paged=False)
+    q = dev(w.q)
+    o1 = decode(pl, q, 1 / 16).cpu().numpy()
+    o2 = decode(pc, q, 1 / 16).cpu().numpy()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert pl.guards_intact()
+    del pl, pc
+    ref = _oracle_by_group(w, lens)
+    assert rel_err_rows(o1, ref) <= TOL
+
+
+def test_dense_decode_three_streams_131072_every_row():
+    """Dense decode over the block-sparse workload's streams (3 x 131072 positions, pages of 256
+    shuffled, 32 q / 4 KV heads, 16 tiles a wave), the launch the benchmark times for context: paged ==
+    contiguous bit for bit, and every row within the bound of the oracle."""
+    L = 131072
+    w = make_workload(5, [L] * 3, 256, 32, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w)
+    q = dev(w.q)
+    o1 = decode(pl, q, 1 / 16).cpu().numpy()
+    del pl
+    pc = Placed(w, paged=False)
+    o2 = decode(pc, q, 1 / 16).cpu().numpy()
+    del pc
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    ref = _oracle_by_group(w, w.lens)
+    assert rel_err_rows(o1, ref) <= TOL
 
 
 def test_workspace_reuse_decode_and_sparse():

@@ -115,9 +115,9 @@ def test_fp8_red_control_swapped_scales():
     assert rel_err_rows(bad, ref) > 10 * TOL
 
 
-def test_fp8_decode_full_size_sampled():
+def test_fp8_decode_full_size_every_row():
     """The measured workload's shape (4 streams x 40960 positions, 32 query / 4 KV heads, pages of 256,
-    shuffled table): paged == contiguous bit for bit and sampled heads against the oracle."""
+    shuffled table): paged == contiguous bit for bit and every (stream, head) row against the oracle."""
     S, L, HQ, HKV, PT = 4, 40960, 32, 4, 256
     rng = np.random.default_rng(41)
     q = f32_to_bf16_bits(rng.standard_normal((S, HQ, D), dtype=np.float32))
@@ -177,13 +177,14 @@ def test_fp8_decode_full_size_sampled():
     P.paged_attn_decode(qd, P.PAGED_BF16, HQ, ckv, cpg, lens, S, L, 1 / 16, out2, ws)
     assert np.array_equal(got.view(np.uint32), out2.cpu().numpy().view(np.uint32)), "paged != contiguous"
     qf = bf16_bits_to_f32(q).astype(np.float64)
-    for s, h in ((0, 0), (1, 13), (2, 22), (3, 31)):
-        g = h // (HQ // HKV)
-        Kd = O.e4m3_dequantize(KC[s, g], KS[s, g])
-        Vd = O.e4m3_dequantize(VC[s, g], VS[s, g])
-        ref = O.decode(qf[s:s + 1, h:h + 1], Kd[None, None], Vd[None, None], [L], 1 / 16)[0, 0]
-        err = rel_err_rows(got[s, h][None], ref[None])
-        assert err <= TOL, (s, h, err)
+    G = HQ // HKV
+    for s in range(S):
+        for g in range(HKV):
+            Kd = O.e4m3_dequantize(KC[s, g], KS[s, g])
+            Vd = O.e4m3_dequantize(VC[s, g], VS[s, g])
+            ref = O.decode(qf[s:s + 1, g * G:(g + 1) * G], Kd[None, None], Vd[None, None], [L], 1 / 16)[0]
+            err = rel_err_rows(got[s, g * G:(g + 1) * G], ref)
+            assert err <= TOL, (s, g, err)
 
 
 def _sparse(pl, q, hq, ids, cnt, k, max_len):

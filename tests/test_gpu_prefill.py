@@ -99,15 +99,18 @@ def test_prefill_8192_in_chunks_of_2048_sampled():
         assert rel_err_rows(o1[rows], ref[rows]) <= TOL, c0
 
 
-def test_prefill_40960_in_chunks_of_2048_sampled():
+def test_prefill_40960_in_chunks_of_2048():
     """The 40960-token prompt (160 shuffled pages of 256, 32 q / 4 KV heads) as twenty 2048-query
-    chunks, the launches the benchmark times: every chunk paged == contiguous bit for bit, and
-    sampled rows of the first, a middle and the last chunk against the oracle."""
+    chunks, the launches the benchmark times: every chunk paged == contiguous bit for bit.  In the
+    first and the last chunk, one query of every 16-query block (the queries of one workgroup), at a
+    rotating place inside the block so that every wave's rows come up, is checked on all 32 heads
+    against the oracle: every workgroup of those launches is covered.  A middle chunk is sampled."""
     n = 40960
     w = make_workload(4, [n], 256, 32, 4, dtype="bf16", table_kind="shuffled", n_queries=n)
     pl, pc = Placed(w), Placed(w, paged=False)
     Kf, Vf = w.as_f64("K")[0], w.as_f64("V")[0]
     rng = np.random.default_rng(1)
+    per_block = np.arange(0, 2048, 16) + (np.arange(128) % 16)
     for c0 in range(0, n, 2048):
         qc = np.ascontiguousarray(w.q[c0:c0 + 2048])
         q = dev(qc)
@@ -115,8 +118,12 @@ def test_prefill_40960_in_chunks_of_2048_sampled():
         oc = _prefill(pc, q, 2048, c0).cpu().numpy()
         assert np.array_equal(o1.view(np.uint32), oc.view(np.uint32)), c0
         assert np.isfinite(o1).all(), c0
-        if c0 in (0, 20480, n - 2048):
+        if c0 in (0, n - 2048):
+            rows = per_block
+        elif c0 == 20480:
             rows = np.unique(np.concatenate([[0, 2047], rng.integers(0, 2048, 6)]))
-            qf = (qc.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            ref = O.prefill(qf, Kf, Vf, c0, 1 / 16, rows=rows)
-            assert rel_err_rows(o1[rows], ref[rows]) <= TOL, c0
+        else:
+            continue
+        qf = (qc.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = O.prefill(qf, Kf, Vf, c0, 1 / 16, rows=rows)
+        assert rel_err_rows(o1[rows], ref[rows]) <= TOL, c0

@@ -91,18 +91,26 @@ def test_window_fp8_matches_oracle_and_paged_equals_contiguous():
     assert rel_err_rows(got, ref) <= TOL
 
 
-def test_window_full_size_sampled():
+def test_window_full_size_every_row():
     """4 streams x 40960 positions, 32 q / 4 KV heads, pages of 256 shuffled, a window of 2 (16 columns):
-    sampled rows against the oracle."""
+    paged == contiguous bit for bit, and every one of the 256 (stream, query, head) rows against the
+    oracle."""
     S, L, HQ, HKV, W = 4, 40960, 32, 4, 2
+    G = HQ // HKV
     w = make_workload(96, [L] * S, 256, HQ, HKV, dtype="bf16", table_kind="shuffled")
     rng = np.random.default_rng(196)
     q = f32_to_bf16_bits(rng.standard_normal((S, W, HQ, D), dtype=np.float32))
     pl = Placed(w, paged=True)
     got = _window(pl, dev(q), HQ, W, pl.lens, S, L, "bf16").cpu().numpy()
+    del pl
+    pc = Placed(w, paged=False)
+    got_c = _window(pc, dev(q), HQ, W, pc.lens, S, L, "bf16").cpu().numpy()
+    del pc
+    assert np.array_equal(got.view(np.uint32), got_c.view(np.uint32))
     qf = bf16_bits_to_f32(q).astype(np.float64)
-    K, V = w.as_f64("K"), w.as_f64("V")
-    for s, k, h in ((0, 0, 0), (1, 1, 9), (3, 0, 31), (2, 1, 20)):
-        g = h // 8
-        ref = O.decode_window(qf[s:s + 1, :, h:h + 1], K[s:s + 1, g:g + 1], V[s:s + 1, g:g + 1], [L], 1 / 16)
-        assert rel_err_rows(got[s, k, h][None], ref[0, k, 0][None]) <= TOL, (s, k, h)
+    for s in range(S):
+        for g in range(HKV):
+            K = bf16_bits_to_f32(w.K[s:s + 1, g:g + 1]).astype(np.float64)
+            V = bf16_bits_to_f32(w.V[s:s + 1, g:g + 1]).astype(np.float64)
+            ref = O.decode_window(qf[s:s + 1, :, g * G:(g + 1) * G], K, V, [L], 1 / 16)[0]
+            assert rel_err_rows(got[s, :, g * G:(g + 1) * G], ref) <= TOL, (s, g)
