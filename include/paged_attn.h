@@ -31,8 +31,9 @@
  * Ownership ([P2 maintainer replies: drain before anything is freed, fills on
  * the engine stream]): the caller allocates and owns every buffer (inputs,
  * arena, table, lengths, outputs, workspace).  The library allocates nothing,
- * frees nothing, keeps no global state, reads no environment variable and
- * never synchronises: all work is enqueued on `stream`.  Inputs are only read.
+ * frees nothing, keeps no global state (one exception: the scratch array of
+ * paged_attn_decode_noalloc, below), reads no environment variable and never
+ * synchronises: all work is enqueued on `stream`.  Inputs are only read.
  * The caller must not free, reuse or re-table pages until `stream` has drained.
  * Structs are passed by host pointer and read only during the call.
  *
@@ -75,7 +76,8 @@ enum {
   PAGED_EUNSUPPORTED = -2, /* a valid request this library does not serve      */
   PAGED_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
   PAGED_EHIP = -4,         /* a HIP launch failed                               */
-  PAGED_EFULL = -5         /* no free page or run: the request waits (page pool) */
+  PAGED_EFULL = -5,        /* no free page or run: the request waits (page pool) */
+  PAGED_ESCRATCH = -6      /* the request needs more scratch than paged_attn_decode_noalloc holds */
 };
 
 /* The pages' Pg argument ([P1 "What this changes"]). */
@@ -133,6 +135,31 @@ int paged_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
                       float scale, float *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t paged_attn_decode_workspace(int32_t n_streams, int32_t n_q_heads, int32_t max_len);
+
+/* ------------------------------------------------------------------------ */
+/* Dense decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments, results and refusals are those of
+ * paged_attn_decode, and the output is bit for bit the same; the split partials
+ * go to a scratch array of PAGED_NOALLOC_SCRATCH_BYTES (16,908,288 bytes: the
+ * partials of 1024 (stream, q head) rows at the most splits a stream takes, so
+ * 32 streams x 32 q heads fit at any length) that the library keeps in each
+ * GPU's memory for the life of the process.  No allocation is made by this call.
+ *   - PAGED_ESCRATCH when paged_attn_decode_workspace(n_streams, n_q_heads,
+ *     max_len) exceeds that size.
+ *   - The first call on a device, with that device current, looks up the device
+ *     address of that GPU's array (no stream work, no allocation); `stream` must
+ *     belong to the current device.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in time on
+ *     one GPU (two streams, or two threads) race on it and must be ordered by the
+ *     caller.  Its contents are undefined between calls; nothing in it has to
+ *     start at zero.
+ */
+#define PAGED_NOALLOC_SCRATCH_BYTES (1024u * 16u * (256u + 2u) * 4u)
+int paged_attn_decode_noalloc(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                              const paged_kv *kv, const paged_pg *pg,
+                              const int32_t *seq_lens, int32_t n_streams, int32_t max_len,
+                              float scale, float *out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Windowed decode ([P1 "What this changes" names fn_attn_chunks_ahead beside

@@ -28,6 +28,8 @@ PAGED_EUNSUPPORTED = -2
 PAGED_EWORKSPACE = -3
 PAGED_EHIP = -4
 PAGED_EFULL = -5
+PAGED_ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 1024 * 16 * (256 + 2) * 4  # PAGED_NOALLOC_SCRATCH_BYTES
 
 
 class PagedError(RuntimeError):
@@ -52,6 +54,8 @@ _SIGS = {
     "paged_attn_decode": (c_int32, [c_void_p, c_int32, c_int32, POINTER(KvStruct), POINTER(PgStruct), c_void_p,
                                     c_int32, c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "paged_attn_decode_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
+    "paged_attn_decode_noalloc": (c_int32, [c_void_p, c_int32, c_int32, POINTER(KvStruct), POINTER(PgStruct),
+                                            c_void_p, c_int32, c_int32, c_float, c_void_p, c_void_p]),
     "paged_attn_decode_window": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(KvStruct),
                                            POINTER(PgStruct), c_void_p, c_int32, c_int32, c_float, c_void_p,
                                            c_void_p, c_size_t, c_void_p]),
@@ -161,6 +165,13 @@ def paged_attn_decode(q, q_dtype: int, n_q_heads: int, kv: KvStruct, pg: PgStruc
     _check(lib().paged_attn_decode(_p(q), q_dtype, n_q_heads, ctypes.byref(kv), ctypes.byref(pg), _p(seq_lens),
                                    n_streams, max_len, scale, _p(out), _p(workspace), wb, _stream(stream)),
            "paged_attn_decode")
+
+
+def paged_attn_decode_noalloc(q, q_dtype: int, n_q_heads: int, kv: KvStruct, pg: PgStruct, seq_lens, n_streams: int,
+                              max_len: int, scale: float, out, stream=None):
+    _check(lib().paged_attn_decode_noalloc(_p(q), q_dtype, n_q_heads, ctypes.byref(kv), ctypes.byref(pg),
+                                           _p(seq_lens), n_streams, max_len, scale, _p(out), _stream(stream)),
+           "paged_attn_decode_noalloc")
 
 
 def paged_attn_decode_window_workspace(n_streams: int, n_q_heads: int, n_window: int, max_len: int) -> int:

@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "paged_attn.h"
 #include "internal.h"
 
@@ -76,10 +79,13 @@ size_t dec_ws(int32_t n_streams, int32_t n_q_heads, int64_t max_keys) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PAGED_OK : PAGED_EHIP; }
 
-// Decode, sparse decode (ids != NULL) and the windowed decode (nq > 1 queries a stream).
-int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq, const paged_kv* kv,
-                  const paged_pg* pg, const int32_t* lens, const int32_t* ids, int32_t k, int32_t n_streams,
-                  int32_t max_len, float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Decode, sparse decode (ids != NULL) and the windowed decode (nq > 1 queries a stream): checks the
+// request and fills `a` except its workspace pointers; *need = the workspace bytes it takes.  With
+// n_streams == 0 there is nothing to launch (PAGED_OK, *need = 0).
+int decode_prepare(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq, const paged_kv* kv,
+                   const paged_pg* pg, const int32_t* lens, const int32_t* ids, int32_t k, int32_t n_streams,
+                   int32_t max_len, float scale, float* out, DecArgs* a, size_t* need) {
+  *need = 0;
   if (n_streams < 0 || max_len < 0 || max_len > MAX_POS || nq < 1) return PAGED_EINVAL;
   int r = check_kv(kv, pg);
   if (r) return r;
@@ -102,38 +108,56 @@ int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq,
     if (k < 1 || !al(ids, 4) || (int64_t)k * 4 > MAX_POS) return PAGED_EINVAL;
     max_keys = (int64_t)4 * k;
   }
-  const size_t need = dec_ws(n_streams, n_q_heads * nq, max_keys);
-  if (ws_bytes < need || (need > 0 && (ws == nullptr || !al(ws, 16)))) return PAGED_EWORKSPACE;
+  *need = dec_ws(n_streams, n_q_heads * nq, max_keys);
 
-  DecArgs a;
-  a.q = q;
-  a.kb = (const char*)kv->k;
-  a.vb = (const char*)kv->v;
+  a->q = q;
+  a->kb = (const char*)kv->k;
+  a->vb = (const char*)kv->v;
   const bool fp8 = kv->dtype == PAGED_FP8_E4M3;
-  a.ksb = fp8 ? (const char*)kv->k_scale : nullptr;
-  a.vsb = fp8 ? (const char*)kv->v_scale : nullptr;
-  a.pg = to_dev(pg, kv->dtype);
-  a.lens = lens;
-  a.ids = ids;
-  a.ids_stride = ids ? k : 0;
-  a.max_len = max_len;
-  a.hq = n_q_heads;
-  a.hkv = kv->n_kv_heads;
-  a.nq = nq;
-  a.kvshift = 0;
-  a.zscale = (float)((double)scale * 1.4426950408889634);
-  int ns = dec_splits_max((int)max_keys);
-  a.ns_max = ns < 1 ? 1 : ns;
-  const size_t rows = (size_t)n_streams * n_q_heads * nq * a.ns_max;
+  a->ksb = fp8 ? (const char*)kv->k_scale : nullptr;
+  a->vsb = fp8 ? (const char*)kv->v_scale : nullptr;
+  a->pg = to_dev(pg, kv->dtype);
+  a->lens = lens;
+  a->ids = ids;
+  a->ids_stride = ids ? k : 0;
+  a->max_len = max_len;
+  a->hq = n_q_heads;
+  a->hkv = kv->n_kv_heads;
+  a->nq = nq;
+  a->kvshift = 0;
+  a->zscale = (float)((double)scale * 1.4426950408889634);
+  const int ns = dec_splits_max((int)max_keys);
+  a->ns_max = ns < 1 ? 1 : ns;
+  a->part_o = nullptr;
+  a->part_ml = nullptr;
+  a->out = out;
+  return PAGED_OK;
+}
+
+// Carves the split partials out of `ws` (16-byte aligned, at least the prepared need) and launches.
+int decode_launch(DecArgs& a, int32_t q_dtype_rows, void* ws, int32_t n_streams, hipStream_t stream) {
+  const size_t rows = (size_t)n_streams * a.hq * a.nq * a.ns_max;
   a.part_o = (float*)ws;
   a.part_ml = (float*)((char*)a.part_o + rows * HD * sizeof(float));
-  a.out = out;
-  const int elem = fp8 ? 2 : kv->dtype == PAGED_BF16 ? 1 : 0;
-  const int G = n_q_heads / kv->n_kv_heads;
+  const bool fp8 = q_dtype_rows == PAGED_FP8_E4M3;
+  const int elem = fp8 ? 2 : q_dtype_rows == PAGED_BF16 ? 1 : 0;
+  const int G = a.hq / a.hkv;
   // Windows and e4m3 rows take the MFMA decode (e4m3 decode is bound by the vector units there); one
   // query over bf16 or float32 rows takes the vector-ALU decode.
-  if (nq > 1 || fp8) return hip_status(launch_decode_mfma(a, elem, G, n_streams, stream));
+  if (a.nq > 1 || fp8) return hip_status(launch_decode_mfma(a, elem, G, n_streams, stream));
   return hip_status(launch_decode(a, elem, G, n_streams, stream));
+}
+
+int decode_common(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq, const paged_kv* kv,
+                  const paged_pg* pg, const int32_t* lens, const int32_t* ids, int32_t k, int32_t n_streams,
+                  int32_t max_len, float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DecArgs a;
+  size_t need = 0;
+  const int r = decode_prepare(q, q_dtype, n_q_heads, nq, kv, pg, lens, ids, k, n_streams, max_len, scale, out, &a,
+                               &need);
+  if (r || n_streams == 0) return r;
+  if (ws_bytes < need || (need > 0 && (ws == nullptr || !al(ws, 16)))) return PAGED_EWORKSPACE;
+  return decode_launch(a, kv->dtype, ws, n_streams, stream);
 }
 
 int rows_common(int gather, void* lin, int64_t ss, int64_t sh, int64_t sp, void* region, int32_t n_heads,
@@ -167,6 +191,34 @@ int rows_common(int gather, void* lin, int64_t ss, int64_t sh, int64_t sp, void*
   return hip_status(launch_rows(a, stream));
 }
 
+// ---- scratch of the allocation-free decode -------------------------------------------------
+// One array a GPU, in the library's own device memory (it lives as long as the process), for callers
+// that cannot allocate.  Host code never passes `scratch` itself to a kernel or a copy: on the host
+// that name stands for a host-side shadow, not the device array.  Its device address is looked up
+// once a device, with that device current, and kept in scratch_dev.
+static __device__ __align__(256) char scratch[PAGED_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_dev[MAX_DEVICES];
+std::mutex scratch_mu;
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return PAGED_EHIP;
+  void* p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_dev[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PAGED_EHIP;
+      scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PAGED_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +232,21 @@ int paged_attn_decode(const void* q, int32_t q_dtype, int32_t n_q_heads, const p
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(q, q_dtype, n_q_heads, 1, kv, pg, seq_lens, nullptr, 0, n_streams, max_len, scale, out,
                        workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_noalloc(const void* q, int32_t q_dtype, int32_t n_q_heads, const paged_kv* kv,
+                              const paged_pg* pg, const int32_t* seq_lens, int32_t n_streams, int32_t max_len,
+                              float scale, float* out, hipStream_t stream) {
+  DecArgs a;
+  size_t need = 0;
+  int r = decode_prepare(q, q_dtype, n_q_heads, 1, kv, pg, seq_lens, nullptr, 0, n_streams, max_len, scale, out, &a,
+                         &need);
+  if (r || n_streams == 0) return r;
+  if (need > (size_t)PAGED_NOALLOC_SCRATCH_BYTES) return PAGED_ESCRATCH;
+  void* ws = nullptr;
+  r = scratch_of_current_device(&ws);
+  if (r) return r;
+  return decode_launch(a, kv->dtype, ws, n_streams, stream);
 }
 
 size_t paged_attn_decode_window_workspace(int32_t n_streams, int32_t n_q_heads, int32_t n_window, int32_t max_len) {
@@ -420,6 +487,7 @@ const char* paged_strerror(int status) {
     case PAGED_EWORKSPACE: return "workspace missing or too small";
     case PAGED_EHIP: return "HIP launch failed";
     case PAGED_EFULL: return "no free page or run (the request waits)";
+    case PAGED_ESCRATCH: return "request needs more than the allocation-free decode's scratch";
     default: return "unknown status";
   }
 }

@@ -219,3 +219,20 @@ def test_bench_refuses_more_than_one_gpu():
         assert r.returncode == 2, (argv, r.returncode, r.stderr[-500:])
         assert "one GPU" in r.stderr
         assert r.stdout == ""
+
+
+def test_noalloc_refusals_come_before_any_device_work():
+    """The allocation-free decode refuses what paged_attn_decode refuses, and a request whose split
+    partials would not fit its scratch (PAGED_ESCRATCH), before looking up any device memory."""
+    kv, pg = _kv(), _pg()
+
+    def call(hq=32, S=4, max_len=40960, q=FAKE):
+        return B.lib().paged_attn_decode_noalloc(q, B.PAGED_BF16, hq, ctypes.byref(kv), ctypes.byref(pg), FAKE, S,
+                                                 max_len, 0.0625, FAKE, 0)
+    assert call(S=64) == B.PAGED_ESCRATCH          # the partials of 64 x 32 heads x 16 splits do not fit
+    assert P.paged_attn_decode_workspace(64, 32, 40960) > B.NOALLOC_SCRATCH_BYTES
+    assert P.paged_attn_decode_workspace(32, 32, 40960) <= B.NOALLOC_SCRATCH_BYTES
+    assert call(hq=30) == B.PAGED_EINVAL
+    assert call(q=MIS) == B.PAGED_EINVAL
+    assert call(S=0) == B.PAGED_OK
+    assert "scratch" in P.strerror(B.PAGED_ESCRATCH)
