@@ -229,13 +229,17 @@ int paged_pool_blocks(const void *ik, void *pooled, int32_t idx_dim, int32_t are
 /* Block scores and top-k selection ([P1 "What this changes": fn_qsa_scores reads
  * pooled rows through pg_at; four-head QSA scores]).
  *
- * score[s][b] = sum over indexer heads h, then dimensions d, of qi[s][h][d] * pooled[s][b][d],
- * accumulated in float64 in that order (each product is exact), for the
+ * score[s][b] = sum over indexer heads h and dimensions d of qi[s][h][d] * pooled[s][b][d] in
+ * float64, in this order: q[d] = sum over h of qi[s][h][d], head by head; each product
+ * pooled[s][b][d] * q[d] rounded to float64; the products added in 8 groups (group j: the
+ * 4-dim chunks c = j, j+8, j+16, ..., dims 4c .. 4c+3, in increasing dim order) whose sums meet
+ * as ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)); for the
  * nb_s = min(seq_lens[s], max_len) / 4 complete blocks.  Then the k blocks with
  * the highest score (lower id first among equal scores; -0.0 == +0.0) are
  * written ascending to out_ids[s][0 .. n-1] with n = min(k, nb_s); the rest of
  * the row is filled with -1 and out_count[s] = n.
- *   qi         device [n_streams][n_idx_heads][idx_dim], qi_dtype
+ *   qi         device [n_streams][n_idx_heads][idx_dim], qi_dtype; idx_dim a multiple of 4, at
+ *              most 1024, n_idx_heads x idx_dim at most 2048
  *   pooled     device, pooled region base (float32 rows, see paged_pool_blocks);
  *              arena_dtype is the arena's K/V type, which gives page_elems its byte size
  *   out_scores optional device [n_streams][max_len/4] float64 (NULL: kept in workspace); entries

@@ -366,19 +366,31 @@ def scores(qI: np.ndarray, pooled: np.ndarray) -> np.ndarray:
     indexer query with the block's pooled row, in float64.
 
     qI [Hi][DI] exact values (float64), pooled [nb][DI] float32.
-    Accumulation order (the pages fix none; this is the reading): one float64
-    accumulator per block, terms
-    added head by head and, within a head, dimension by dimension.  Every
-    product of a bf16 query and a float32 pooled value is exact in float64, so
-    the only roundings are those of the additions, in this order.
+    Order (the pages fix none; this is the reading).  In exact arithmetic
+    sum_h sum_d qI[h,d] p[d] = sum_d (sum_h qI[h,d]) p[d], so the queries are
+    first summed over the heads, head by head, into q[d]; every product
+    p[d] * q[d] is rounded to float64; the products are added in 8 groups, group
+    j holding the dims of the 4-dim chunks c = j, j+8, j+16, ... (dims 4c .. 4c+3)
+    in increasing dim order from 0; and the 8 group sums meet in the fixed tree
+    ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)).  Only the rounding order is
+    chosen; the value is the definition's to float64 precision.
     """
     P = pooled.astype(np.float64)
-    acc = np.zeros(P.shape[0], dtype=np.float64)
+    nb = P.shape[0]
     Hi, DI = qI.shape
+    q = np.zeros(DI, dtype=np.float64)
     for h in range(Hi):
-        for d in range(DI):
-            acc = acc + qI[h, d] * P[:, d]
-    return acc
+        q = q + qI[h]
+    prod = P * q[None, :]
+    groups = []
+    for j in range(8):
+        acc = np.zeros(nb, dtype=np.float64)
+        for c in range(j, (DI + 3) // 4, 8):
+            for d in range(4 * c, min(4 * c + 4, DI)):
+                acc = acc + prod[:, d]
+        groups.append(acc)
+    g = groups
+    return ((g[0] + g[1]) + (g[2] + g[3])) + ((g[4] + g[5]) + (g[6] + g[7]))
 
 
 def topk(score: np.ndarray, k: int) -> np.ndarray:

@@ -351,7 +351,8 @@ int paged_block_scores_topk(const void* qi, int32_t qi_dtype, int32_t n_idx_head
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(qi_dtype) || !dtype_ok(arena_dtype)) return PAGED_EINVAL;
   if (n_streams < 0 || max_len < 0 || max_len > MAX_POS || k < 1) return PAGED_EINVAL;
-  if (n_idx_heads < 1 || idx_dim < 4 || idx_dim % 4 != 0 || (int64_t)n_idx_heads * idx_dim > 2048) return PAGED_EINVAL;
+  if (n_idx_heads < 1 || idx_dim < 4 || idx_dim > 1024 || idx_dim % 4 != 0 || (int64_t)n_idx_heads * idx_dim > 2048)
+    return PAGED_EINVAL;
   int r = check_pg(pg, arena_dtype, max_len, true);
   if (r) return r;
   if (n_streams == 0) return PAGED_OK;

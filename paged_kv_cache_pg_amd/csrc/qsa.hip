@@ -58,212 +58,123 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Scores: a workgroup is one wave and owns 64 consecutive blocks, one a lane.
-// Each lane runs one float64 accumulator over its block's pooled row, head by
-// head and dimension by dimension (the order the definition states), with the
-// indexer queries widened to float64 in LDS and read by broadcast.  Each
-// product of a bf16 / fp32 query and a fp32 pooled value is exact in float64,
-// so the fused and unfused forms agree and the only roundings are the
-// additions, in order.
-//
-// 128-dim rows (scores_kernel128): the wave issues all 32 of its coalesced
-// 16-byte loads (two rows a load, 32 lanes a row) in two rounds of 32 rows and
-// moves the rows into each lane's registers through LDS (17 KB, so two waves
-// fit a SIMD and every block of a 3 x 32768 workload is resident at once).
-// Other widths stage 64 rows of up to 128 dims at a time.
+// Scores.  In exact arithmetic sum_h sum_d qI[h][d] p[d] = sum_d q[d] p[d] with q[d] = sum_h qI[h][d],
+// so the workgroup first sums the indexer queries over the heads (float64, head by head) into LDS.
+// A block is then scored by 8 lanes: lane j of the block takes the 4-dim chunks c = j, j+8, j+16, ...
+// of its pooled row (so the 8 lanes of a block read 128 contiguous bytes a load), adds each product
+// p[d] * q[d] (rounded to float64, not fused) to its float64 sum in increasing dim order, and the 8
+// lane sums meet in a fixed butterfly, ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)) (float64 addition
+// commutes, so every lane of the block ends with the same value).  This is the order of the oracle's
+// definition, so scores are bit for bit the oracle's.
+// A wave scores 8 blocks a round and R rounds (2 for 128-wide rows), all of whose row loads are issued
+// before the first sum; a workgroup is 4 waves.  The stream's length and the table entries of a
+// lane's blocks are requested together, then the rows; the queries are summed while the rows are in
+// flight.
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int SC_NB = 64;                 // blocks a workgroup
-constexpr int SC_DCH = 128;               // dims a staged chunk (generic kernel)
-constexpr int SC_ROWB = SC_DCH * 4 + 16;  // LDS bytes a staged row (pad: consecutive rows 4 banks apart)
+constexpr int SC_THREADS = 256;
+constexpr int SC_LPB = 8;                      // lanes a block
+constexpr int SC_MAXD = 1024;                  // dims at most
 
 // The first workgroup of each stream clears the stream's coarse top-k histogram (the
 // histogram kernel, launched next on the same stream, adds into it).
 __device__ __forceinline__ void zero_hist(const TopkArgs& a, int s) {
   uint4* h = (uint4*)(a.hist + (int64_t)s * 4096);
-  for (int i = threadIdx.x; i < 4096 / 4; i += SC_NB) h[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < 4096 / 4; i += SC_THREADS) h[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// q[d] = sum over heads of the stream's indexer queries, float64, head by head, for d < idx_dim.
 template <bool QBF16>
-__device__ __forceinline__ void widen_q(const TopkArgs& a, int s, double* s_q) {
+__device__ __forceinline__ void sum_queries(const TopkArgs& a, int s, double* s_q) {
+#pragma clang fp contract(off)
   const int m = a.n_idx_heads * a.idx_dim;
-  for (int i = threadIdx.x; i < m; i += SC_NB) {
-    if constexpr (QBF16) {
-      const uint16_t u = ((const uint16_t*)a.qi)[(int64_t)s * m + i];
-      s_q[i] = (double)__uint_as_float((uint32_t)u << 16);
-    } else {
-      s_q[i] = (double)((const float*)a.qi)[(int64_t)s * m + i];
+  for (int d = threadIdx.x; d < a.idx_dim; d += SC_THREADS) {
+    double q = 0.0;
+    for (int h = 0; h < a.n_idx_heads; ++h) {
+      const int64_t i = (int64_t)s * m + h * a.idx_dim + d;
+      const double v = QBF16 ? (double)__uint_as_float((uint32_t)((const uint16_t*)a.qi)[i] << 16)
+                             : (double)((const float*)a.qi)[i];
+      q = q + v;
     }
+    s_q[d] = q;
   }
 }
 
-// 128-dim rows: n_idx_heads x 128 query values (at most 2048), 16 bytes a lane at a time.  The
-// loads are issued by q128_load and widened into LDS by q128_store, so that the caller can put other
-// loads between them.  A chunk past the queries re-reads the last one (a uniform test skips the
-// rounds no lane needs) and is not stored.
-constexpr int SC_QCH = 2048 / 4 / SC_NB;  // 16-byte query chunks a lane at most
-template <bool QBF16>
-__device__ __forceinline__ void q128_load(const TopkArgs& a, int s, uint4 (&v)[SC_QCH]) {
-  constexpr int PER = QBF16 ? 8 : 4;  // values a 16-byte chunk
-  const int m = a.n_idx_heads * 128;
-  const int nch = m / PER;
-  const uint4* src = (const uint4*)((const char*)a.qi + (int64_t)s * m * (QBF16 ? 2 : 4));
-#pragma unroll
-  for (int j = 0; j < SC_QCH; ++j)
-    if (j * SC_NB < nch) v[j] = src[min((int)threadIdx.x + j * SC_NB, nch - 1)];
-}
-template <bool QBF16>
-__device__ __forceinline__ void q128_store(const TopkArgs& a, const uint4 (&v)[SC_QCH], double* s_q) {
-  constexpr int PER = QBF16 ? 8 : 4;
-  const int nch = a.n_idx_heads * 128 / PER;
-#pragma unroll
-  for (int j = 0; j < SC_QCH; ++j) {
-    const int c = threadIdx.x + j * SC_NB;
-    if (c < nch) {
-      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-      double* d = s_q + c * PER;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (QBF16) {
-          d[2 * e] = (double)__uint_as_float(w[e] << 16);
-          d[2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
-        } else {
-          d[e] = (double)__uint_as_float(w[e]);
-        }
-      }
-    }
-  }
-}
-
-template <bool QBF16>
-__global__ __launch_bounds__(SC_NB, 2) void scores_kernel128(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_stage[32 * SC_ROWB];
-  extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x 128], dynamic
-  __shared__ int64_t s_base[SC_NB];
-  const int s = blockIdx.y, lane = threadIdx.x;
+// NCH: 4-dim chunks a lane at most (idx_dim <= 32 NCH); R: rounds of 8 blocks a wave.
+template <bool QBF16, int NCH, int R>
+__global__ __launch_bounds__(SC_THREADS) void scores_kernel(TopkArgs a) {
+  // the products are rounded before they are added (no fused multiply-add): float32 queries summed over
+  // heads can carry more than 29 bits, and then a product is not exact in float64
+#pragma clang fp contract(off)
+  __shared__ __attribute__((aligned(16))) double s_q[SC_MAXD];
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & (SC_LPB - 1), slot = lane >> 3;
+  constexpr int BPW = 8 * R;                          // blocks a wave
+  const int b_wg = blockIdx.x * (SC_THREADS / 64) * BPW;
+  const int b_wave = b_wg + w * BPW;
   if (blockIdx.x == 0) zero_hist(a, s);
-  // This lane's table entry (every block below max_blocks has one), the queries and the stream's
-  // length are all requested before any of them is used, so they take one round trip: the entry
-  // is read without a branch (from the length when there is no table, and then not used), and
-  // the length, which is wanted first, is requested last.  A lane's row base is used only for
-  // rows below the length.
-  const int b0 = blockIdx.x * SC_NB;
-  const int b = b0 + lane;
+  // The stream's length and the table entries of this lane's blocks are requested together (every
+  // block below max_blocks has an entry; an entry is used as an address only below the length).
   const bool paged = a.pg.table != nullptr;
-  const int p = 4 * min(b, a.max_blocks - 1);
-  const uint32_t lp = (uint32_t)p / (uint32_t)a.pg.ptok;
-  const int32_t* tp = paged ? a.pg.table + (int64_t)s * a.pg.stride + lp : a.lens + s;
-  const int32_t entry = *tp;
-  uint4 qv[SC_QCH];
-  q128_load<QBF16>(a, s, qv);
-  const int len = a.lens[s];
-  const int nb = min(max(len, 0), a.max_blocks * 4) >> 2;
-  if (b0 >= nb) return;
-  const int64_t page = paged ? (int64_t)entry : (int64_t)s;
-  const int within = paged ? p - (int)lp * a.pg.ptok : p;
-  s_base[lane] = page * a.pg.page_bytes + (int64_t)(within >> 2) * (128 * 4);
-  q128_store<QBF16>(a, qv, s_q);
-  const int nrows = min(SC_NB, nb - b0);
-  __syncthreads();
-
-  // Rows move in two rounds of 32 (rows 0-31, then 32-63): lane (r1, ch) loads 16-byte chunk ch
-  // (dims 4ch .. 4ch+3) of rows 2i + r1.  The second round's loads are issued before the first
-  // round's rows are read out of LDS, so they are in flight meanwhile.
-  const int r1 = lane >> 5, ch = lane & 31;
-  auto load_round = [&](int rd, u32x4 (&v)[16]) {
+  int32_t entry[R];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * rd + 2 * i + r1;  // rows past nrows re-read row 0
-      v[i] = *(const u32x4*)(a.pooled + s_base[r < nrows ? r : 0] + ch * 16);
-    }
-  };
-  auto store_round = [&](const u32x4 (&v)[16]) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) *(u32x4*)(s_stage + (2 * i + r1) * SC_ROWB + ch * 16) = v[i];
-  };
-  float4 row[32];  // this lane's row: dims 4c .. 4c+3 in row[c]
-  u32x4 va[16], vb[16];
-  load_round(0, va);
-  store_round(va);
-  load_round(1, vb);
-  __syncthreads();
-  if (lane < 32) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) row[c] = *(const float4*)(s_stage + lane * SC_ROWB + c * 16);
+  for (int r = 0; r < R; ++r) {
+    const int b = min(b_wave + 8 * r + slot, a.max_blocks - 1);
+    entry[r] = paged ? a.pg.table[(int64_t)s * a.pg.stride + (uint32_t)(4 * b) / (uint32_t)a.pg.ptok] : 0;
   }
-  __syncthreads();
-  store_round(vb);
-  __syncthreads();
-  if (lane >= 32) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) row[c] = *(const float4*)(s_stage + (lane - 32) * SC_ROWB + c * 16);
-  }
-  if (b >= nb) return;
-  double acc = 0.0;
-  for (int h = 0; h < a.n_idx_heads; ++h) {
-    const double* qh = s_q + h * 128;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      // widen the row in place each head: hoisted out of the head loop, the 128 doubles would
-      // not fit beside everything else
-      asm volatile("" : "+v"(row[c].x), "+v"(row[c].y), "+v"(row[c].z), "+v"(row[c].w));
-      const double2 q01 = *(const double2*)(qh + 4 * c);
-      const double2 q23 = *(const double2*)(qh + 4 * c + 2);
-      acc = __fma_rn(q01.x, (double)row[c].x, acc);
-      acc = __fma_rn(q01.y, (double)row[c].y, acc);
-      acc = __fma_rn(q23.x, (double)row[c].z, acc);
-      acc = __fma_rn(q23.y, (double)row[c].w, acc);
-    }
-  }
-  a.scores[(int64_t)s * a.max_blocks + b] = acc;
-}
-
-template <bool QBF16>
-__global__ __launch_bounds__(SC_NB) void scores_kernel(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_rows[SC_NB * SC_ROWB];
-  extern __shared__ __attribute__((aligned(16))) double s_q[];  // [heads x dims], dynamic
-  __shared__ int64_t s_base[SC_NB];
-  const int s = blockIdx.y, lane = threadIdx.x;
-  if (blockIdx.x == 0) zero_hist(a, s);
   const int nb = min(max(a.lens[s], 0), a.max_blocks * 4) >> 2;
-  const int b0 = blockIdx.x * SC_NB;
-  if (b0 >= nb) return;
-  widen_q<QBF16>(a, s, s_q);
+  if (b_wg >= nb) return;                             // the whole workgroup is past the blocks
+  const int nch = (a.idx_dim + 3) >> 2;               // 4-dim chunks a row
   const int rowb = a.idx_dim * 4;
-  const int b = b0 + lane;
-  const int nrows = min(SC_NB, nb - b0);
-  s_base[lane] = pool_at(a.pg, s, b < nb ? b : b0, rowb);
-  __syncthreads();
-
-  const int nch = (a.idx_dim + SC_DCH - 1) / SC_DCH;
-  double acc = 0.0;
-  for (int h = 0; h < a.n_idx_heads; ++h) {
-    for (int c = 0; c < nch; ++c) {
-      const int d0 = c * SC_DCH, wd = min(SC_DCH, a.idx_dim - d0);
-      if (nch > 1 || h == 0) {
-        if (nch > 1) __syncthreads();  // every lane is done with the previous chunk
-        const int cpr = wd / 4;        // 16-byte chunks a row
-        for (int it = lane; it < nrows * cpr; it += SC_NB) {
-          const int r = it / cpr, cc = it - r * cpr;
-          *(u32x4*)(s_rows + r * SC_ROWB + cc * 16) = *(const u32x4*)(a.pooled + s_base[r] + (int64_t)d0 * 4 + cc * 16);
-        }
-        __syncthreads();
-      }
-      if (b < nb) {
-        const char* rw = s_rows + lane * SC_ROWB;
-        const double* qh = s_q + h * a.idx_dim + d0;
-        for (int d = 0; d < wd; d += 4) {
-          const float4 p = *(const float4*)(rw + d * 4);
-          acc = __fma_rn(qh[d + 0], (double)p.x, acc);
-          acc = __fma_rn(qh[d + 1], (double)p.y, acc);
-          acc = __fma_rn(qh[d + 2], (double)p.z, acc);
-          acc = __fma_rn(qh[d + 3], (double)p.w, acc);
-        }
-      }
+  // Row loads of every round (blocks past nb, and chunks past the row, re-read chunk 0 of block
+  // 0 of the stream, which exists).
+  auto row_base = [&](int b, int32_t e) -> int64_t {
+    const int p = 4 * b;
+    const int within = paged ? p - (int)((uint32_t)p / (uint32_t)a.pg.ptok) * a.pg.ptok : p;
+    const int64_t page = paged ? (int64_t)e : (int64_t)s;
+    return page * a.pg.page_bytes + (int64_t)(within >> 2) * rowb;
+  };
+  const char* first = a.pooled + pool_at(a.pg, s, 0, rowb);
+  u32x4 v[R][NCH];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int b = b_wave + 8 * r + slot;
+    const char* base = a.pooled + row_base(b < nb ? b : 0, entry[r]);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = j + SC_LPB * i;
+      const char* src = (b < nb && c < nch) ? base + c * 16 : first;
+      v[r][i] = *(const u32x4*)src;
     }
   }
-  if (b < nb) a.scores[(int64_t)s * a.max_blocks + b] = acc;
+  // the queries summed over heads into LDS while the rows are in flight
+  sum_queries<QBF16>(a, s, s_q);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = j + SC_LPB * i;
+      if (c < nch) {
+        const double2 q01 = *(const double2*)(s_q + 4 * c);
+        const double2 q23 = *(const double2*)(s_q + 4 * c + 2);
+        const float p[4] = {__uint_as_float(v[r][i].x), __uint_as_float(v[r][i].y), __uint_as_float(v[r][i].z),
+                            __uint_as_float(v[r][i].w)};
+        const double q[4] = {q01.x, q01.y, q23.x, q23.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * c + e < a.idx_dim) acc = acc + (double)p[e] * q[e];
+      }
+    }
+    acc = acc + __shfl_xor(acc, 1);
+    acc = acc + __shfl_xor(acc, 2);
+    acc = acc + __shfl_xor(acc, 4);
+    const int b = b_wave + 8 * r + slot;
+    if (j == 0 && b < nb) a.scores[(int64_t)s * a.max_blocks + b] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,19 +944,30 @@ size_t topk_workspace_bytes(int n_streams, int max_blocks, int k, int scores_ext
   return b;
 }
 
+template <bool QBF16, int NCH, int R>
+void launch_scores_t(const TopkArgs& a, int n_streams, hipStream_t st) {
+  constexpr int per_wg = (SC_THREADS / 64) * 8 * R;
+  dim3 grid((a.max_blocks + per_wg - 1) / per_wg, n_streams);
+  hipLaunchKernelGGL((scores_kernel<QBF16, NCH, R>), grid, dim3(SC_THREADS), 0, st, a);
+}
+
+template <bool QBF16>
+void launch_scores(const TopkArgs& a, int n_streams, hipStream_t st) {
+  const int nch = (a.idx_dim + 3) / 4;  // 4-dim chunks a row; a lane takes ceil(nch / 8)
+  if (nch <= 8) launch_scores_t<QBF16, 1, 4>(a, n_streams, st);
+  else if (nch <= 16) launch_scores_t<QBF16, 2, 2>(a, n_streams, st);
+  else if (nch <= 32) launch_scores_t<QBF16, 4, 2>(a, n_streams, st);
+  else if (nch <= 64) launch_scores_t<QBF16, 8, 1>(a, n_streams, st);
+  else if (nch <= 128) launch_scores_t<QBF16, 16, 1>(a, n_streams, st);
+  else launch_scores_t<QBF16, 32, 1>(a, n_streams, st);
+}
+
 hipError_t launch_scores_topk(const TopkArgs& a, bool qi_bf16, int n_streams, hipStream_t st) {
   if (n_streams <= 0) return hipSuccess;
   hipError_t e;
   if (a.max_blocks > 0) {
-    dim3 grid((a.max_blocks + SC_NB - 1) / SC_NB, n_streams);
-    const size_t qbytes = (size_t)a.n_idx_heads * a.idx_dim * sizeof(double);
-    if (a.idx_dim == 128) {
-      if (qi_bf16) hipLaunchKernelGGL(scores_kernel128<true>, grid, dim3(SC_NB), qbytes, st, a);
-      else hipLaunchKernelGGL(scores_kernel128<false>, grid, dim3(SC_NB), qbytes, st, a);
-    } else {
-      if (qi_bf16) hipLaunchKernelGGL(scores_kernel<true>, grid, dim3(SC_NB), qbytes, st, a);
-      else hipLaunchKernelGGL(scores_kernel<false>, grid, dim3(SC_NB), qbytes, st, a);
-    }
+    if (qi_bf16) launch_scores<true>(a, n_streams, st);
+    else launch_scores<false>(a, n_streams, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -133,6 +133,8 @@ def test_sparse_pool_topk_refusals():
                                      0, FAKE, wt, 0) == E                            # k = 0
     assert L.paged_block_scores_topk(FAKE, 1, 32, 128, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 512, FAKE,
                                      FAKE, 0, FAKE, wt, 0) == E                      # 32 x 128 > 2048
+    assert L.paged_block_scores_topk(FAKE, 1, 1, 1028, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 512, FAKE,
+                                     FAKE, 0, FAKE, wt, 0) == E                      # rows past 1024 dims
     assert L.paged_block_scores_topk(FAKE, 1, 4, 128, FAKE, 1, ctypes.byref(pg5), FAKE, 3, 131072, 512, FAKE, FAKE,
                                      0, FAKE, wt - 8, 0) == B.PAGED_EWORKSPACE
 

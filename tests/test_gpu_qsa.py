@@ -356,22 +356,32 @@ def test_topk_stream_past_the_selection_bitmap():
 
 
 def test_scores_sum_order_matches_oracle():
-    """Indexer keys (1, 2^60, -2^60, 0, ...) in every row and queries chosen so that only one float64
-    accumulator run head by head, dim by dim gives the oracle's value (0, 0, 1 for the three
-    streams); any other order of the additions would give 1, 1, 1 or lose the 1."""
-    lens = [64, 64, 64]
-    w = make_workload(68, lens, 16, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=2)
+    """Pooled rows and queries built so that the order of the float64 additions decides the score
+    (2^60 absorbs a 1 added after it): the kernel must take the oracle's order -- queries summed over
+    heads first, products in 8 groups by 4-dim chunk, each group in increasing dims, the groups
+    meeting in the tree ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)).  Six streams, each with one
+    crafted row in every block, give 1, 0, 1, 0, 1, 0 in that order and other orders would not."""
     big = 2.0 ** 60
+    lens = [64] * 6
+    w = make_workload(68, lens, 16, 1, 1, dtype="bf16", table_kind="shuffled", idx_dim=128, n_idx_heads=3)
+    rows = [{4: 1.0, 32: big, 33: -big},       # groups: g1 = 1, g0 = 0             -> 1
+            {0: 1.0, 32: big, 33: -big},       # in-group order: (1 + 2^60) - 2^60   -> 0
+            {0: 1.0, 8: big, 12: -big},        # tree pairs: (1 + 0) + (2^60 - 2^60) -> 1
+            {0: big, 4: 1.0, 16: -big},        # halves: (2^60 + 1) + (-2^60)        -> 0
+            {0: 1.0, 4: 1.0},                  # heads first (queries below)         -> 1
+            {0: 1.0}]                          # heads in order (queries below)      -> 0
     IK = np.zeros(w.IK.shape, np.float32)
-    IK[:, :, 0], IK[:, :, 1], IK[:, :, 2] = 1.0, big, -big
+    for s, r in enumerate(rows):
+        for d, x in r.items():
+            IK[s, :, d] = x
     w.IK = f32_to_bf16_bits(IK)
     qI = np.zeros(w.qI.shape, np.float32)
-    qI[0, 0, :3] = 1.0                                  # one head: (1 + 2^60) - 2^60 = 0
-    qI[1, 0, 0], qI[1, 1, 1], qI[1, 1, 2] = 1.0, 1.0, 1.0  # head 0 then head 1: 0
-    qI[2, 0, 1], qI[2, 0, 2], qI[2, 1, 0] = 1.0, 1.0, 1.0  # heads swapped: 1
+    qI[:4, 0, :] = 1.0
+    qI[4, 0, 0], qI[4, 1, 4], qI[4, 2, 4] = 1.0, big, -big
+    qI[5, 0, 0], qI[5, 1, 0], qI[5, 2, 0] = big, 1.0, -big
     w.qI = f32_to_bf16_bits(qI)
     pl = Placed(w)
-    S, ml, k = 3, 64, 4
+    S, ml, k = 6, 64, 4
     b0 = dev(np.zeros(S, np.int32))
     b1 = dev(np.array([L // 4 for L in lens], np.int32))
     P.paged_pool_blocks(pl.ik, pl.pooled, 128, P.PAGED_BF16, pl.pg, b0, b1, S, ml)
@@ -379,11 +389,12 @@ def test_scores_sum_order_matches_oracle():
     cnt = torch.empty(S, dtype=torch.int32, device="cuda")
     sc = torch.zeros((S, ml // 4), dtype=torch.float64, device="cuda")
     ws = torch.empty(P.paged_topk_workspace(S, ml, k), dtype=torch.uint8, device="cuda")
-    P.paged_block_scores_topk(dev(w.qI), P.PAGED_BF16, 2, 128, pl.pooled, P.PAGED_BF16, pl.pg, pl.lens, S, ml, k,
+    P.paged_block_scores_topk(dev(w.qI), P.PAGED_BF16, 3, 128, pl.pooled, P.PAGED_BF16, pl.pg, pl.lens, S, ml, k,
                               ids, cnt, sc, ws)
     torch.cuda.synchronize()
     sc = sc.cpu().numpy()
-    assert np.all(sc[0] == 0.0) and np.all(sc[1] == 0.0) and np.all(sc[2] == 1.0)
+    for s, want in enumerate([1.0, 0.0, 1.0, 0.0, 1.0, 0.0]):
+        assert np.all(sc[s] == want), (s, sc[s])
     pooled = O.pool(w.as_f64("IK"), lens)
     for s in range(S):
         assert np.array_equal(sc[s], O.scores(w.as_f64("qI")[s], pooled[s])), s

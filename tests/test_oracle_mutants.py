@@ -42,6 +42,33 @@ def _head_modulo(q, K, V, lens, scale):
     return _decode(q, K[:, idx], V[:, idx], lens, scale)
 
 
+def _scores_one_accumulator(qI, pooled):
+    """One float64 accumulator per block, head by head and dim by dim."""
+    P = pooled.astype(np.float64)
+    acc = np.zeros(P.shape[0])
+    for h in range(qI.shape[0]):
+        for d in range(qI.shape[1]):
+            acc = acc + qI[h, d] * P[:, d]
+    return acc
+
+
+def _scores_groups_in_sequence(qI, pooled):
+    """The stated heads-first sum and 8 chunk groups, but the groups added one after the other."""
+    P = pooled.astype(np.float64)
+    q = np.zeros(qI.shape[1])
+    for h in range(qI.shape[0]):
+        q = q + qI[h]
+    prod = P * q[None, :]
+    total = np.zeros(P.shape[0])
+    for j in range(8):
+        acc = np.zeros(P.shape[0])
+        for c in range(j, (qI.shape[1] + 3) // 4, 8):
+            for d in range(4 * c, min(4 * c + 4, qI.shape[1])):
+                acc = acc + prod[:, d]
+        total = total + acc
+    return total
+
+
 def _topk_ties_high(score, k):
     order = sorted(range(len(score)), key=lambda b: (-score[b], -b))
     return np.sort(np.array(order[:min(k, len(score))], dtype=np.int64))
@@ -71,6 +98,9 @@ DECODE_PINS = [T.test_decode_single_key_is_value_row, T.test_decode_zero_query_i
                T.test_decode_two_keys_logistic_closed_form, T.test_decode_gqa_head_map_is_division,
                T.test_decode_dominant_key_and_affine_equivariance, T.test_decode_empty_stream_is_zero, *BRUTE]
 
+SCORES_PINS = [T.test_scores_exact_on_integers_and_linear_in_heads,
+               T.test_scores_sum_order_heads_first_then_eight_groups_and_a_tree]
+
 MUTANTS = {
     "decode drops the scale": ("decode", lambda q, K, V, lens, scale: _decode(q, K, V, lens, 1.0), DECODE_PINS),
     "decode doubles the scale": ("decode", lambda q, K, V, lens, scale: _decode(q, K, V, lens, 2 * scale), DECODE_PINS),
@@ -94,11 +124,11 @@ MUTANTS = {
                           [T.test_pool_closed_forms, T.test_pool_of_short_stream_is_empty]),
     "scores sum the dims backwards": ("scores", lambda qI, pooled:
                                       _scores(np.ascontiguousarray(qI[:, ::-1]), np.ascontiguousarray(pooled[:, ::-1])),
-                                      [T.test_scores_exact_on_integers_and_linear_in_heads,
-                                       T.test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim]),
-    "scores sum the heads first": ("scores", lambda qI, pooled: _scores(qI.sum(axis=0, keepdims=True), pooled),
-                                   [T.test_scores_exact_on_integers_and_linear_in_heads,
-                                    T.test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim]),
+                                      SCORES_PINS),
+    "scores in one accumulator head by head": ("scores", _scores_one_accumulator, SCORES_PINS),
+    "scores groups added in sequence": ("scores", _scores_groups_in_sequence, SCORES_PINS),
+    "scores drop a head": ("scores", lambda qI, pooled: _scores(qI[:-1], pooled) if len(qI) > 1 else _scores(qI, pooled),
+                           SCORES_PINS),
     "top-k ties go to the higher id": ("topk", _topk_ties_high, [T.test_topk_matches_python_sort_and_ties]),
     "top-k ids in score order": ("topk", _topk_score_order, [T.test_topk_matches_python_sort_and_ties]),
     "row offset one row off": ("row_offset", lambda *a, **k: _row_offset(*a, **k) + a[6],

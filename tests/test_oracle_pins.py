@@ -283,20 +283,41 @@ def test_scores_exact_on_integers_and_linear_in_heads():
     assert np.array_equal(O.scores(qs, pooled), got)
 
 
-def test_scores_sum_order_is_one_accumulator_head_by_head_dim_by_dim():
-    """Terms chosen so that the order of the float64 additions decides the result: one accumulator
-    over head 0's dims, then head 1's, keeps 0; summing each head apart first, or the dims in
-    another order, keeps 1 (2^60 absorbs a 1 added after it, so only what precedes it is lost)."""
+def test_scores_sum_order_heads_first_then_eight_groups_and_a_tree():
+    """Terms chosen so that the order of the float64 additions decides the result (2^60 absorbs a 1
+    added after it, so only what precedes it is lost): the queries are summed over heads first, the
+    products fall into 8 groups by 4-dim chunk (chunk c in group c mod 8), each group adds its dims
+    in increasing order, and the groups meet in the tree ((g0 + g1) + (g2 + g3)) + (...)."""
     big = 2.0 ** 60
-    pooled = np.array([[1.0, big, -big]], np.float32)          # one block, 3 dims
-    # one head: 1 + 2^60 -> 2^60, then - 2^60 -> 0 (the dims in reverse order would give 1)
-    assert O.scores(np.array([[1.0, 1.0, 1.0]]), pooled)[0] == 0.0
-    # two heads: head 0 contributes only dim 0 (1), head 1 only dims 1, 2 (2^60, -2^60):
-    # one accumulator: (1 + 2^60) - 2^60 = 0; per-head sums first: 1 + (2^60 - 2^60) = 1
-    q2 = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 1.0]])
-    assert O.scores(q2, pooled)[0] == 0.0
-    # heads swapped: (0 + 2^60 - 2^60) + 1 = 1 in the stated order
-    assert O.scores(q2[::-1].copy(), pooled)[0] == 1.0
+    DI = 64                                   # 16 chunks: group j holds chunks j and j + 8
+    one = np.ones((1, DI))
+
+    def row(**vals):
+        p = np.zeros((1, DI), np.float32)
+        for k, v in vals.items():
+            p[0, int(k[1:])] = v
+        return p
+    # groups, not one accumulator: dim 4 (group 1) = 1; dims 32, 33 (both group 0) = 2^60, -2^60.
+    # group sums 0 and 1 give 1; one accumulator over dims 0..63 gives (1 + 2^60) - 2^60 = 0
+    assert O.scores(one, row(d4=1.0, d32=big, d33=-big))[0] == 1.0
+    # inside a group, increasing dims: dims 0 (1), 32 (2^60), 33 (-2^60), all group 0: 0; the
+    # chunks of a group in another order (chunk 8 first) would keep the 1
+    assert O.scores(one, row(d0=1.0, d32=big, d33=-big))[0] == 0.0
+    # the tree pairs (g0 + g1) and (g2 + g3): g0 = 1, g2 = 2^60, g3 = -2^60 give 1 + 0 = 1; the groups
+    # added in sequence would give ((1 + 0) + 2^60) - 2^60 = 0
+    assert O.scores(one, row(d0=1.0, d8=big, d12=-big))[0] == 1.0
+    # and the halves (g0..g3) + (g4..g7): g0 = 2^60, g1 = 1, g4 = -2^60 give 2^60 + (-2^60) = 0 after
+    # the 1 is absorbed in the left half; pairing g1 with g4's half first would keep it
+    assert O.scores(one, row(d0=big, d4=1.0, d16=-big))[0] == 0.0
+    # heads first: head 0 puts 1 on dim 0, heads 1 and 2 put 2^60 and -2^60 on dim 4, so q[4] = 0 and
+    # the score is 1; adding head by head into one accumulator would give (1 + 2^60) - 2^60 = 0
+    qI = np.zeros((3, DI))
+    qI[0, 0], qI[1, 4], qI[2, 4] = 1.0, big, -big
+    assert O.scores(qI, row(d0=1.0, d4=1.0))[0] == 1.0
+    # the heads in order: q[0] = (2^60 + 1) - 2^60 = 0 when head 1 adds the 1 after 2^60
+    qI = np.zeros((3, DI))
+    qI[0, 0], qI[1, 0], qI[2, 0] = big, 1.0, -big
+    assert O.scores(qI, row(d0=1.0))[0] == 0.0
 
 
 def test_topk_matches_python_sort_and_ties():
