@@ -788,6 +788,7 @@ def run_page_pool():
 
 
 def run_decode(args):
+    import torch
     dec = DecodeBench()
     with ClockSampler() as clk:
         ms_step, wall = time_steps(dec.step, args.steps, args.warmup)
@@ -812,6 +813,62 @@ def run_decode(args):
         "page_runs": run_rows(dec, args),
     }
     del dec
+    torch.cuda.empty_cache()
+    out["decode_batch_shapes"] = run_decode_batches(args)
+    return out
+
+
+def run_decode_batches(args, streams=(1, 2, 3, 5, 8)):
+    """The headline decode's shape (40960 positions a stream, pages of 256 shuffled, 32 q / 4 KV heads,
+    bf16) at other batch sizes.  Every page of the arena holds N(0,1) bf16 rows drawn on the device;
+    enough arena copies rotate between steps that the 256 MB Infinity Cache cannot serve a step from
+    the previous one.  One (stream, head) row of each shape is checked against the oracle."""
+    import numpy as np
+    import torch
+    import oracle as O
+    import paged_kv_cache_pg_amd as P
+    from paged_kv_cache_pg_amd.inputs import make_table
+    L, PT, HQ, HKV, D = 40960, 256, 32, 4, 256
+    lay = P.ArenaLayout(HKV, D, PT, P.PAGED_BF16)
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    out = {}
+    for S in streams:
+        table_np, n_pages = make_table("shuffled", [L // PT] * S, np.random.default_rng(100 + S))
+        table = torch.from_numpy(table_np.astype(np.int32)).cuda()
+        pg = P.make_pg(table, PT, lay.page_elems)
+        arena_bytes = n_pages * lay.page_bytes
+        copies = max(2, -(-600_000_000 // arena_bytes))
+        arenas = [torch.randn(arena_bytes // 2, generator=gen, device="cuda").to(torch.bfloat16) for _ in range(copies)]
+        kvs = [P.make_kv(a.data_ptr() + lay.k_off, a.data_ptr() + lay.v_off, P.PAGED_BF16, HKV, D) for a in arenas]
+        q = torch.randn((S, HQ, D), generator=gen, device="cuda").to(torch.bfloat16)
+        lens = torch.full((S,), L, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(P.paged_attn_decode_workspace(S, HQ, L), dtype=torch.uint8, device="cuda")
+        o = torch.empty((S, HQ, D), dtype=torch.float32, device="cuda")
+
+        def step(i):
+            P.paged_attn_decode(q, P.PAGED_BF16, HQ, kvs[i % copies], pg, lens, S, L, 1 / 16, o, ws)
+        ms, _ = time_steps(step, args.steps, args.warmup)
+        nbytes = S * HKV * L * D * 2 * 2 + q.numel() * 2 + table.numel() * 4 + S * 4 + o.numel() * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        # one row against the oracle: the last stream's last head, its rows read back through the table
+        step(0)
+        torch.cuda.synchronize()
+        s, h = S - 1, HQ - 1
+        g = h // (HQ // HKV)
+        a0 = arenas[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        pe = lay.page_elems
+        Kr = np.concatenate([a0[int(table_np[s, lp]) * pe + (lay.k_off // 2) + g * PT * D:][:PT * D] for lp in range(L // PT)])
+        Vr = np.concatenate([a0[int(table_np[s, lp]) * pe + (lay.v_off // 2) + g * PT * D:][:PT * D] for lp in range(L // PT)])
+        f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        qf = q[s:s + 1, h:h + 1].float().cpu().numpy().astype(np.float64)
+        ref = O.decode(qf, f64(Kr).reshape(1, 1, L, D), f64(Vr).reshape(1, 1, L, D), [L], 1 / 16)[0, 0]
+        got = o[s, h].cpu().numpy()
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        out[str(S)] = {"streams": S, "us_per_step": round(ms * 1e3, 2), "alg_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "arena_copies": copies, "oracle_row_rel_err": err}
+        log(f"decode {S} x {L}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%}); row err {err:.1e}")
+        del arenas, kvs, a0
+        torch.cuda.empty_cache()
     return out
 
 
@@ -922,7 +979,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "decode_fp8", "prefill", "sparse", "append"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode_batches", "decode_fp8", "prefill", "sparse", "append"],
+                    default=None,
                     help="run one row only (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -952,6 +1010,8 @@ def main():
     if args.only in (None, "decode"):
         result.update(run_decode(args))
         torch.cuda.empty_cache()
+    if args.only == "decode_batches":
+        result["decode_batch_shapes"] = run_decode_batches(args)
     if args.only in (None, "decode_fp8"):
         result["decode_e4m3"] = run_decode_fp8(args)
         torch.cuda.empty_cache()

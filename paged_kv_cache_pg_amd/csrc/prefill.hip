@@ -23,7 +23,10 @@
 //                 accumulators, with P split into bf16 hi + lo so P keeps ~16 bits).
 // One barrier a tile: K and V live in two LDS buffers each; the loads of tile t+1 go from
 // global memory straight into LDS (no registers), issued at the start of iteration t into the
-// buffers tile t-1 left, and are waited for at its end.  Workgroups of one KV head are spread
+// buffers tile t-1 left, and are waited for at its end.  The four buffers are separate LDS
+// objects and the tile loop is unrolled by two, so that every access names its buffer: with one
+// array indexed by tile parity the compiler could not tell a tile's loads from its reads and
+// waited for the next tile's loads before the first K read.  Workgroups of one KV head are spread
 // round-robin so that consecutive workgroups (one per XCD) share KV heads two XCDs apiece.
 #include "internal.h"
 #include "mfma.h"
@@ -69,8 +72,13 @@ constexpr float RESCALE_SLACK = 8.f;  // log2 units a row's running max may lag 
 template <int G>
 __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel(PreArgs a) {
   constexpr int QB = PF_ROWS / G;  // queries a workgroup
-  __shared__ __attribute__((aligned(16))) char s_k[2][TILEB];
-  __shared__ __attribute__((aligned(16))) char s_v[2][TILEB];
+  // two K and two V buffers, four separate LDS objects: the compiler can then tell the buffer a
+  // tile's loads land in from the one the tile reads, and does not wait for the former before
+  // reading the latter
+  __shared__ __attribute__((aligned(16))) char s_k0[TILEB];
+  __shared__ __attribute__((aligned(16))) char s_k1[TILEB];
+  __shared__ __attribute__((aligned(16))) char s_v0[TILEB];
+  __shared__ __attribute__((aligned(16))) char s_v1[TILEB];
   __shared__ int64_t s_keyat[2][PF_KT];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, u = l >> 4, c16 = l & 15;
@@ -206,20 +214,20 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
   stage_keyat(1, key_page(1));
   int32_t page_next = key_page(2);
   __syncthreads();
-  load_tile(0, s_k[0], s_v[0]);
+  load_tile(0, s_k0, s_v0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
+  // Tile t reads kcur / vcur and loads tile t+1 into knext / vnext (the buffers tile t-1 left).
+  auto tile = [&](int t, const char* kcur, const char* vcur, char* knext, char* vnext) {
     const int k0 = t * PF_KT;
-    // K(t+1), V(t+1) into the buffers tile t-1 left; they land during this iteration and are
-    // waited for at its end
-    if (t + 1 < nt) load_tile(t + 1, s_k[(t + 1) & 1], s_v[(t + 1) & 1]);
+    // K(t+1), V(t+1) land during this tile and are waited for at its end
+    if (t + 1 < nt) load_tile(t + 1, knext, vnext);
     stage_keyat(t + 2, page_next);
     page_next = key_page(t + 3);
 
     f32x4 s_cur[KB][RB];
-    qk(s_k[t & 1], s_cur);
+    qk(kcur, s_cur);
 
     bf16x8 phi[NS2][RB], plo[NS2][RB];  // [32-key step][rb]
     float alpha_rb[RB];
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
     // Fragments are read PV_AHEAD steps ahead.
     {
       constexpr int PV_AHEAD = PAGED_PF_PV_AHEAD;
-      const char* vbuf = s_v[t & 1];
+      const char* vbuf = vcur;
       auto vfrag = [&](int s2, int db) {
         const int o = voff[db & 7] + 256 * (db >> 3) + 32 * ROWB * s2;
         const bf16x4 v1 = lds_tr16(vbuf, o);
@@ -355,6 +363,11 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
     // ---- K(t+1) and V(t+1) have landed; every wave is done with K(t) and V(t) ----
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  // two tiles an iteration, so that each buffer is a fixed LDS object in each call
+  for (int t = 0; t < nt; t += 2) {
+    tile(t, s_k0, s_v0, s_k1, s_v1);
+    if (t + 1 < nt) tile(t + 1, s_k1, s_v1, s_k0, s_v0);
   }
 
   // ---- normalise and write: lane holds O^T[16db + 4u + i][row 16rb + c16] ----
