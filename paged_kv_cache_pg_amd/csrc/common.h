@@ -25,6 +25,13 @@ __device__ __forceinline__ int32_t pg_page(const PgDev& pg, int s, int p) {
   return s;
 }
 
+// The word a lookup of pg_page reads: the table entry of position p of stream s, or `dummy` (any
+// readable word, its value then unused) when there is no table, so that the load can be issued
+// with no branch around it.
+__device__ __forceinline__ const int32_t* pg_entry(const PgDev& pg, int s, int p, const int32_t* dummy) {
+  return pg.table != nullptr ? pg.table + ((int64_t)s * pg.stride + (uint32_t)p / (uint32_t)pg.ptok) : dummy;
+}
+
 // Byte offset of row (h, p) inside `page`, for a region whose page part is [H][ptok][row_bytes].
 __device__ __forceinline__ int64_t pg_offset(const PgDev& pg, int32_t page, int h, int p, int row_bytes) {
   const int within = pg.table != nullptr ? (int)((uint32_t)p % (uint32_t)pg.ptok) : p;

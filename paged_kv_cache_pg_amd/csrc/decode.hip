@@ -33,13 +33,7 @@ namespace {
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PAGED_DEC_RING
-#define PAGED_DEC_RING 2         // 4-key steps of K/V buffered a lane
-#endif
-#ifndef PAGED_DEC_RING_SHORT
-#define PAGED_DEC_RING_SHORT 4   // the same for streams of at most two tiles a wave
-#endif
-#ifndef PAGED_DEC_WG_PER_CU
-#define PAGED_DEC_WG_PER_CU 1    // workgroups a CU the register budget is set for
+#define PAGED_DEC_RING 4         // 4-key steps of bf16 K/V buffered a lane (float32 rows: 2)
 #endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -187,7 +181,7 @@ struct StepBuf {
 };
 
 template <int ET, int G, int RING>
-__global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
   using RT = Rows<ET>;
   constexpr int ROWB = RT::ROWB;     // bytes a K/V row
   constexpr int QROWB = RT::QROWB;   // bytes a q row
@@ -233,13 +227,25 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   const int j32 = lane & 31, half = lane >> 5;
   const int max_blocks = a.max_len >> 2;
 
+  // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
+  const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * QROWB;
+
   // Key ids: key (tile tt, lane) is position i = (t_begin + tt) * 64 + lane (dense) or 4 * ids[i / 4] + i % 4
   // (sparse); -1 when masked.  The id and table loads are issued early and finished later so that their
   // latency hides behind the steps in flight; every index is clamped so each load reads valid memory.
+  // Both are issued whether or not there is an id list or a table (reading the q row instead): a load
+  // under a branch leaves the compiler unsure how many loads follow it, and its wait for that load
+  // becomes a wait for every load in flight.
   auto load_id = [&](int tt) -> int {
-    if (a.ids == nullptr) return 0;
     const int i = (t_begin + tt) * TILE + lane;
-    return a.ids[(int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0)];
+    const int32_t* p = a.ids != nullptr ? a.ids + ((int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0))
+                                        : (const int32_t*)qrow;
+    const int v = *p;
+    return a.ids != nullptr ? v : 0;
+  };
+  auto load_page = [&](int pos) -> int32_t {
+    const int32_t e = *pg_entry(a.pg, s, pos >= 0 ? pos : 0, (const int32_t*)qrow);
+    return a.pg.table != nullptr ? e : s;
   };
   auto key_pos = [&](int tt, int id) -> int {
     const int i = (t_begin + tt) * TILE + lane;
@@ -247,9 +253,6 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
     if (a.ids == nullptr) return i;
     return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
   };
-
-  // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
-  const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * QROWB;
 
   // Loads of global step gs = SPT * tt + i: i < NSTEP is K step i of tile tt, else V step i - NSTEP.
   // Every load is issued (masked keys and steps past the wave's tiles read the q row instead) so none
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
-      const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
+      const int32_t page0 = load_page(pos0);
       s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
     }
     int id_next = load_id(1);
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(WGS, PAGED_DEC_WG_PER_CU) void decode_split_kernel(
       // key_ids -> key_at for tile t+1: one table lookup a key, written four steps later and first
       // needed DEPTH steps before tile t+1 starts
       const int pos1 = key_pos(t + 1, id_next);
-      const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
+      const int32_t page1 = load_page(pos1);
       id_next = load_id(t + 2);
 
 #pragma unroll
@@ -491,20 +494,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
 
-// Ring depth: one step ahead keeps the register file small for long streams, where every wave has
-// several tiles and two waves share a SIMD; streams of at most two tiles a wave (short or sparse
-// key lists) run their few steps three ahead instead.  The depth changes only when loads are
-// issued, never the arithmetic, so results do not depend on it.
+// Ring depth: bf16 rows keep three steps in flight a wave (one more step or one fewer was slower on
+// every batch shape measured); float32 rows, twice the registers a step, keep one.  The depth
+// changes only when loads are issued, never the arithmetic, so results do not depend on it.
 template <int ET, int G>
 hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
-  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
-  const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
   if constexpr (ET == ET_BF16) {
-    if (short_keys)
-      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING_SHORT>), grid, dim3(WGS), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<ET, G, 2>), grid, dim3(WGS), 0, st, a);
   }
@@ -513,14 +510,34 @@ hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
   return launch_decode_combine(a, n_streams, st);
 }
 
-// Short key lists (at most two tiles a wave) leave most of the GPU idle and each wave waiting on its
-// own loads: there a KV head's q heads are spread over up to 2^PAGED_DEC_HSPLIT workgroups, which read
-// the same K/V rows (the second read mostly from L2), so twice the waves keep loads in flight, each
-// with fewer registers.  float32 rows hold twice the q registers of bf16 rows, so a float32 workgroup
-// takes at most 4 heads (8 would spill): a group of 8 always runs as two workgroups of 4.
+// A KV head's q heads may be spread over up to 2^PAGED_DEC_HSPLIT workgroups, which read the same
+// K/V rows (the later reads mostly from L2) with fewer registers each: more waves keep loads in
+// flight where the grid alone would leave CUs idle.  That is the case for short key lists (at most
+// two tiles a wave), and for batches whose grid is so small that doubling it still fits the CUs in
+// one round (one 8-wave workgroup a CU): 1 or 2 streams at 40960 keys.  A head's arithmetic does
+// not depend on the heads that share its workgroup, so neither does its output.  float32 rows hold
+// twice the q registers of bf16 rows, so a float32 workgroup takes at most 4 heads (8 would spill):
+// a group of 8 always runs as two workgroups of 4.
 #ifndef PAGED_DEC_HSPLIT
 #define PAGED_DEC_HSPLIT 2
 #endif
+
+// CUs of the current device (asked once a device).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev >= 64) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  }
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int ET>
 hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
   constexpr int GMAX = ET == ET_F32 ? 4 : 8;  // heads a workgroup at most
@@ -530,6 +547,9 @@ hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
   a.kvshift = 0;
   if (short_keys) {
     while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1) ++a.kvshift;
+  } else {
+    const long wgs = (long)a.ns_max * a.hkv * n_streams, cus = device_cus();
+    while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1 && (wgs << (a.kvshift + 1)) <= cus) ++a.kvshift;
   }
   while ((G >> a.kvshift) > GMAX) ++a.kvshift;
   switch (G >> a.kvshift) {
