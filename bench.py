@@ -32,8 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_357_492
-DECODE_TRAFFIC_SOURCES = "45502037ee3659c5"
+DECODE_TRAFFIC_BYTES = 676_368_752
+DECODE_TRAFFIC_SOURCES = "a057e2c3912070c3"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
 FP8_TRAFFIC_BYTES = 346_334_423
 FP8_TRAFFIC_SOURCES = "3e1d85c67aecfe95"

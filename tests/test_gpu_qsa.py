@@ -107,6 +107,31 @@ def test_scores_and_topk_bitwise(k):
         assert np.all(ids[s, n:] == -1)
 
 
+def test_topk_workspace_reused_over_shapes():
+    """One workspace over calls of different shapes (a call with more streams than the one before puts
+    its score histograms where the earlier call left selection data): the ids equal the oracle's every
+    time."""
+    cases = ((62, [20000], 300, 256), (61, [8000, 3000, 513], 64, 48), (63, [4000, 4000], 1000, 16),
+             (64, [9000, 100, 7000], 200, 128))
+    need = max(P.paged_topk_workspace(len(lens), max(lens), k) for _, lens, k, _ in cases)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")
+    for seed, lens, k, ptok in cases:
+        w = _qsa_workload(seed, lens, ptok)
+        pl = Placed(w)
+        _pool(pl)
+        S, max_len = w.n_streams, max(w.lens)
+        ids = torch.full((S, k), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.empty(S, dtype=torch.int32, device="cuda")
+        P.paged_block_scores_topk(dev(w.qI), P.PAGED_BF16, HI, DI, pl.pooled, P.PAGED_BF16, pl.pg, pl.lens, S,
+                                  max_len, k, ids, cnt, None, ws)
+        torch.cuda.synchronize()
+        pooled = O.pool(w.as_f64("IK"), w.lens)
+        ids, cnt = ids.cpu().numpy(), cnt.cpu().numpy()
+        for s in range(S):
+            want = O.topk(O.scores(w.as_f64("qI")[s], pooled[s]), k)
+            assert cnt[s] == len(want) and np.array_equal(ids[s, :len(want)], want), (seed, s)
+
+
 def test_topk_exact_ties_lowest_id_wins():
     """Integer-valued indexer keys and queries in {-1, 0, 1}: scores tie exactly and often."""
     w = _qsa_workload(54, [4096, 4096, 2048], 128)
