@@ -125,6 +125,7 @@ int decode_prepare(const void* q, int32_t q_dtype, int32_t n_q_heads, int32_t nq
   a->hkv = kv->n_kv_heads;
   a->nq = nq;
   a->kvshift = 0;
+  a->s0 = 0;
   a->zscale = (float)((double)scale * 1.4426950408889634);
   const int ns = dec_splits_max((int)max_keys);
   a->ns_max = ns < 1 ? 1 : ns;

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
   // blockIdx.y = j * Hkv + gk: the 2^kvshift workgroups of a KV head are Hkv * ns_max ids apart, so
   // with the round-robin placement of workgroups on XCDs (linear id mod 8) they share one XCD's L2
   // whenever Hkv * ns_max is a multiple of 8
-  const int s = blockIdx.z, c = blockIdx.x;
+  const int s = a.s0 + (int)blockIdx.z, c = blockIdx.x;
   const int gk = (int)blockIdx.y % a.hkv;
   const int g = (gk << a.kvshift) | ((int)blockIdx.y / a.hkv);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -497,17 +497,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
 // Ring depth: bf16 rows keep three steps in flight a wave (one more step or one fewer was slower on
 // every batch shape measured); float32 rows, twice the registers a step, keep one.  The depth
 // changes only when loads are issued, never the arithmetic, so results do not depend on it.
+// Launches the split kernel over streams a.s0 .. a.s0 + n - 1.
 template <int ET, int G>
-hipError_t launch_t(const DecArgs& a, int n_streams, hipStream_t st) {
-  dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
+hipError_t launch_split_t(const DecArgs& a, int n, hipStream_t st) {
+  dim3 grid(a.ns_max, a.hkv << a.kvshift, n);
   if constexpr (ET == ET_BF16) {
     hipLaunchKernelGGL((decode_split_kernel<ET, G, PAGED_DEC_RING>), grid, dim3(WGS), 0, st, a);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<ET, G, 2>), grid, dim3(WGS), 0, st, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_decode_combine(a, n_streams, st);
+  return hipGetLastError();
 }
 
 // A KV head's q heads may be spread over up to 2^PAGED_DEC_HSPLIT workgroups, which read the same
@@ -538,27 +537,50 @@ int device_cus() {
   return cus[dev];
 }
 
+// The split kernel over streams a.s0 .. a.s0 + n - 1, with the head split chosen for them.
 template <int ET>
-hipError_t launch_g(const DecArgs& a0, int G, int n_streams, hipStream_t st) {
+hipError_t launch_split_g(const DecArgs& a0, int G, int n, bool short_keys, hipStream_t st) {
   constexpr int GMAX = ET == ET_F32 ? 4 : 8;  // heads a workgroup at most
   DecArgs a = a0;
-  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
-  const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
   a.kvshift = 0;
   if (short_keys) {
     while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1) ++a.kvshift;
   } else {
-    const long wgs = (long)a.ns_max * a.hkv * n_streams, cus = device_cus();
+    const long wgs = (long)a.ns_max * a.hkv * n, cus = device_cus();
     while (a.kvshift < PAGED_DEC_HSPLIT && (G >> a.kvshift) > 1 && (wgs << (a.kvshift + 1)) <= cus) ++a.kvshift;
   }
   while ((G >> a.kvshift) > GMAX) ++a.kvshift;
   switch (G >> a.kvshift) {
-    case 1: return launch_t<ET, 1>(a, n_streams, st);
-    case 2: return launch_t<ET, 2>(a, n_streams, st);
-    case 4: return launch_t<ET, 4>(a, n_streams, st);
-    case 8: if constexpr (GMAX >= 8) return launch_t<ET, 8>(a, n_streams, st); break;
+    case 1: return launch_split_t<ET, 1>(a, n, st);
+    case 2: return launch_split_t<ET, 2>(a, n, st);
+    case 4: return launch_split_t<ET, 4>(a, n, st);
+    case 8: if constexpr (GMAX >= 8) return launch_split_t<ET, 8>(a, n, st); break;
   }
   return hipErrorInvalidValue;
+}
+
+// A batch whose grid takes more than one round of workgroups (one a CU) and ends in a partial round
+// runs as two split launches: the streams of the whole rounds, then the rest, whose smaller grid
+// the head split above can spread over all CUs (5 streams at 40960 keys: 4 + 1).  Every stream's
+// output is the same either way; one combine merges them all.
+template <int ET>
+hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
+  const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
+  const bool short_keys = dec_tps(dec_tiles(max_keys)) <= 2 * NWAVE;
+  const long w = (long)a.ns_max * a.hkv, cus = device_cus();  // workgroups a stream, unsplit
+  int first = n_streams;
+  if (!short_keys && w > 0 && w <= cus) {
+    const int per_round = (int)(cus / w);
+    if (n_streams > per_round && n_streams % per_round != 0) first = n_streams - n_streams % per_round;
+  }
+  hipError_t e = launch_split_g<ET>(a, G, first, short_keys, st);
+  if (e == hipSuccess && first < n_streams) {
+    DecArgs b = a;
+    b.s0 = a.s0 + first;
+    e = launch_split_g<ET>(b, G, n_streams - first, short_keys, st);
+  }
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(a, n_streams, st);
 }
 
 }  // namespace

@@ -26,6 +26,7 @@ struct DecArgs {
   int32_t hkv;
   int32_t nq;             // queries a stream (1, or the window of the windowed decode)
   int32_t kvshift;        // vector-ALU decode: workgroups a KV head = 2^kvshift, each G / 2^kvshift q heads
+  int32_t s0;             // vector-ALU decode: the launch's first stream (stream = s0 + blockIdx.z)
   float zscale;           // softmax scale * log2(e)
   int32_t ns_max;         // split slots a (stream, query, head) in the workspace
   float* part_o;          // [S][nq][Hq][ns_max][HD]

@@ -84,6 +84,28 @@ def test_mixed_pair_concurrent_equals_solo():
         assert np.array_equal(o1.cpu().numpy()[0].view(np.uint32), out[s].view(np.uint32))
 
 
+def test_batch_split_in_two_launches_equals_each_stream_alone():
+    """5 streams of 8192+ keys over 4 KV heads make 5 x 64 workgroups of 8 heads, one round (256 CUs)
+    and a quarter: the first 4 streams run as one launch and the fifth as a second launch whose heads
+    are spread over 4 workgroups each.  Every stream's output equals the stream decoded alone (itself
+    a launch with the heads spread), bit for bit, and the oracle within 2e-3."""
+    lens = [8200, 9000, 8192, 12000, 8500]
+    w = make_workload(12, lens, 256, 32, 4, dtype="bf16", table_kind="shuffled")
+    pl = Placed(w, paged=True)
+    q = dev(w.q)
+    out = decode(pl, q, 1 / 16).cpu().numpy()
+    assert rel_err_rows(out, _oracle(w, 1 / 16)) <= TOL
+    for s in range(len(lens)):
+        table1 = pl.table[s:s + 1].contiguous()
+        pg1 = P.make_pg(table1, w.page_pos, pl.lay.page_elems)
+        ws = torch.zeros(P.paged_attn_decode_workspace(1, 32, w.lens[s]), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((1, 32, 256), dtype=torch.float32, device="cuda")
+        P.paged_attn_decode(q[s:s + 1].contiguous(), P.PAGED_BF16, 32, pl.kv, pg1, pl.lens[s:s + 1].contiguous(), 1,
+                            w.lens[s], 1 / 16, o1, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy()[0].view(np.uint32), out[s].view(np.uint32)), s
+
+
 def test_red_controls():
     """Reading placed pages through a different table, and overwriting one placed row, must each
     change the output."""
