@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 import oracle as O  # noqa: E402
 import paged_kv_cache_pg_amd as P  # noqa: E402
 from paged_kv_cache_pg_amd.inputs import make_workload  # noqa: E402
-from gpu_util import Placed, decode, dev, guarded_out, out_guards_intact, rel_err_rows, TOL  # noqa: E402
+from gpu_util import DT, Placed, decode, dev, guarded_out, out_guards_intact, rel_err_rows, TOL  # noqa: E402
 
 
 def _oracle(w, scale, streams=None):
@@ -84,13 +84,15 @@ def test_mixed_pair_concurrent_equals_solo():
         assert np.array_equal(o1.cpu().numpy()[0].view(np.uint32), out[s].view(np.uint32))
 
 
-def test_batch_split_in_two_launches_equals_each_stream_alone():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_batch_split_in_two_launches_equals_each_stream_alone(dtype):
     """5 streams of 8192+ keys over 4 KV heads make 5 x 64 workgroups of 8 heads, one round (256 CUs)
     and a quarter: the first 4 streams run as one launch and the fifth as a second launch whose heads
-    are spread over 4 workgroups each.  Every stream's output equals the stream decoded alone (itself
-    a launch with the heads spread), bit for bit, and the oracle within 2e-3."""
+    are spread over 4 workgroups each (float32 rows: groups of 8 always run as two workgroups of 4).
+    Every stream's output equals the stream decoded alone (itself a launch with the heads spread),
+    bit for bit, and the oracle within 2e-3."""
     lens = [8200, 9000, 8192, 12000, 8500]
-    w = make_workload(12, lens, 256, 32, 4, dtype="bf16", table_kind="shuffled")
+    w = make_workload(12, lens, 256, 32, 4, dtype=dtype, table_kind="shuffled")
     pl = Placed(w, paged=True)
     q = dev(w.q)
     out = decode(pl, q, 1 / 16).cpu().numpy()
@@ -100,7 +102,7 @@ def test_batch_split_in_two_launches_equals_each_stream_alone():
         pg1 = P.make_pg(table1, w.page_pos, pl.lay.page_elems)
         ws = torch.zeros(P.paged_attn_decode_workspace(1, 32, w.lens[s]), dtype=torch.uint8, device="cuda")
         o1 = torch.empty((1, 32, 256), dtype=torch.float32, device="cuda")
-        P.paged_attn_decode(q[s:s + 1].contiguous(), P.PAGED_BF16, 32, pl.kv, pg1, pl.lens[s:s + 1].contiguous(), 1,
+        P.paged_attn_decode(q[s:s + 1].contiguous(), DT[dtype], 32, pl.kv, pg1, pl.lens[s:s + 1].contiguous(), 1,
                             w.lens[s], 1 / 16, o1, ws)
         torch.cuda.synchronize()
         assert np.array_equal(o1.cpu().numpy()[0].view(np.uint32), out[s].view(np.uint32)), s
