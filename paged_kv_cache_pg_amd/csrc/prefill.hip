@@ -81,7 +81,9 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
   __shared__ __attribute__((aligned(16))) char s_v1[TILEB];
   __shared__ int64_t s_keyat[2][PF_KT];
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, u = l >> 4, c16 = l & 15;
+  // w is read from the first lane so that the compiler knows it is the same across the wave (wave-uniform
+  // LDS addresses, such as the destinations of the global->LDS loads, then stay in scalar registers)
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, u = l >> 4, c16 = l & 15;
   const int nblk = (a.n_q + QB - 1) / QB;
   const int g = blockIdx.x % a.hkv;
   const int qblk = nblk - 1 - (int)(blockIdx.x / a.hkv);  // most work first
@@ -233,29 +235,29 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
     float alpha_rb[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // A tile every row of the block sees whole (below the diagonal) takes no mask, and its
-      // scores are finite, so exp2 needs no -inf test: one multiply, max, subtract, exp2 and add a score.
+      // A tile every row of the block sees whole (below the diagonal) takes no mask; on the others a
+      // masked key's score becomes -inf in place, and exp2(-inf - m) = 0 gives it weight 0, so both
+      // kinds of tile share one max and one exponential loop.
       const bool full = __all(k0 + PF_KT <= lim[rb]);
       float z[KB][4];
-      float mx = NEG_INF;
-      if (full) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            z[kb][i] = s_cur[kb][rb][i] * a.zscale;
-            mx = fmaxf(mx, z[kb][i]);
-          }
-      } else {
+        for (int i = 0; i < 4; ++i) z[kb][i] = s_cur[kb][rb][i] * a.zscale;
+      if (!full) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = k0 + 16 * kb + 4 * u + i;
-            z[kb][i] = key < lim[rb] ? s_cur[kb][rb][i] * a.zscale : NEG_INF;
-            mx = fmaxf(mx, z[kb][i]);
+            z[kb][i] = key < lim[rb] ? z[kb][i] : NEG_INF;
           }
       }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[kb][i]);
       mx = col_max(mx);
       // The reference max moves only when the tile's max passes it by more than RESCALE_SLACK
       // (so P <= 2^RESCALE_SLACK): most tiles leave O untouched.
@@ -263,25 +265,17 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
       const float m_new = move ? fmaxf(m_run[rb], mx) : m_run[rb];
       const float alpha = !move ? 1.f : (m_run[rb] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
       alpha_rb[rb] = alpha;
+      // a row that has seen no key yet keeps m_new = -inf with every score -inf: subtract 0 instead
+      const float m_sub = m_new == NEG_INF ? 0.f : m_new;
       float rs = 0.f;
       float p[KB][4];
-      if (full) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[kb][i] = __builtin_amdgcn_exp2f(z[kb][i] - m_new);
-            rs += p[kb][i];
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[kb][i] = (z[kb][i] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(z[kb][i] - m_new);
-            rs += p[kb][i];
-          }
-      }
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(z[kb][i] - m_sub);
+          rs += p[kb][i];
+        }
       rs = col_sum(rs);
       l_run[rb] = l_run[rb] * alpha + rs;
       m_run[rb] = m_new;
