@@ -13,6 +13,7 @@ _decode, _window, _prefill, _sparse = O.decode, O.decode_window, O.prefill, O.sp
 _pool, _scores, _topk = O.pool, O.scores, O.topk
 _row_offset, _e4m3_value, _e4m3_encode = O.row_offset, O.e4m3_value, O.e4m3_encode
 _pool_row_offset, _place, _gather, _quantize = O.pool_row_offset, O.place, O.gather, O.e4m3_quantize_rows
+_dequantize = O.e4m3_dequantize
 
 
 def _gather_swapped(*a, **k):
@@ -77,6 +78,35 @@ def _topk_ties_high(score, k):
 def _topk_score_order(score, k):
     order = sorted(range(len(score)), key=lambda b: (-score[b], b))
     return np.array(order[:min(k, len(score))], dtype=np.int64)
+
+
+def _prefill_causal_one_late(q, K, V, q_pos0, scale, causal=True, rows=None):
+    """The query at position p also sees key p + 1 (where it is stored)."""
+    if not causal:
+        return _prefill(q, K, V, q_pos0, scale, causal, rows)
+    Nq, Hq, D = q.shape
+    G = Hq // K.shape[0]
+    Lk = q_pos0 + Nq
+    out = np.zeros((Nq, Hq, D))
+    sel = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    for h in range(Hq):
+        g = h // G
+        z = scale * (q[sel, h] @ K[g, :Lk].T)
+        z = np.where(np.arange(Lk)[None, :] > (q_pos0 + sel)[:, None] + 1, -np.inf, z)
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        out[sel, h] = (e @ V[g, :Lk]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def _prefill_head_modulo(q, K, V, q_pos0, scale, causal=True, rows=None):
+    """Query head h reads KV head h mod Hkv instead of h // G."""
+    idx = [h % K.shape[0] for h in range(q.shape[1])]
+    return _prefill(q, K[idx], V[idx], q_pos0, scale, causal, rows)
+
+
+def _topk_one_short(score, k):
+    ids = _topk(score, k)
+    return ids[:-1] if len(ids) else ids
 
 
 def _e4m3_no_saturation(y):
@@ -152,6 +182,20 @@ MUTANTS = {
                                   [F.test_quantize_rows_invariants, F.test_quantize_rows_special_rows]),
     "e4m3 encode does not saturate": ("e4m3_encode", _e4m3_no_saturation,
                                       [F.test_e4m3_encode_ties_go_to_the_even_code_and_large_values_saturate]),
+    "prefill causal mask one key late": ("prefill", _prefill_causal_one_late,
+                                         [T.test_prefill_first_row_and_causal_mask_offsets,
+                                          T.test_prefill_rows_equal_decode_and_chunking_invariance]),
+    "prefill maps heads modulo": ("prefill", _prefill_head_modulo,
+                                  [T.test_prefill_first_row_and_causal_mask_offsets,
+                                   T.test_prefill_rows_equal_decode_and_chunking_invariance]),
+    "sparse rows one position late": ("sparse", lambda q, K, V, ids, scale:
+                                      _sparse(q, np.roll(K, -1, axis=2), np.roll(V, -1, axis=2), ids, scale),
+                                      [T.test_sparse_all_blocks_is_dense_and_subset_is_row_restriction]),
+    "pool over rows one position late": ("pool", lambda IK, lens: _pool(np.roll(IK, -1, axis=1), lens),
+                                         [T.test_pool_closed_forms, T.test_pool_of_short_stream_is_empty]),
+    "top-k returns one id too few": ("topk", _topk_one_short, [T.test_topk_matches_python_sort_and_ties]),
+    "e4m3 dequantize ignores the row scale": ("e4m3_dequantize", lambda codes, scales: _e4m3_value(codes) * 1.0,
+                                              [F.test_quantize_rows_invariants]),
 }
 
 
