@@ -1,6 +1,7 @@
 """float64 CPU oracle for paged KV-cache attention -- test infrastructure only.
 
-Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this package.
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg (the oracle timed on the host and
+the spot checks of sampled rows, both off with --no-cpu-baseline) may import this package.
 """
 from .paged_oracle import (  # noqa: F401
     ESIZE,

@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
 module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
-leg of ``bench.py`` use it.  It shares no code with the HIP library (its own row
+leg of ``bench.py`` (its host timing and its spot checks of sampled rows, both
+off with ``--no-cpu-baseline``) use it.  It shares no code with the HIP library (its own row
 addressing, its own arena layout, its own arithmetic) and is deliberately slow
 and obvious.
 
