@@ -997,6 +997,8 @@ def main():
                     default=None,
                     help="run one row only (for profiler runs)")
     args = ap.parse_args()
+    global ORACLE_LEG
+    ORACLE_LEG = not args.no_cpu_baseline
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -1029,8 +1031,6 @@ def main():
     if args.only in (None, "decode_fp8"):
         result["decode_e4m3"] = run_decode_fp8(args)
         torch.cuda.empty_cache()
-    global ORACLE_LEG
-    ORACLE_LEG = not args.no_cpu_baseline
     want_cpu = args.only is None and not args.no_cpu_baseline
     if args.only in (None, "prefill"):
         result["prefill"] = run_prefill(args, cpu_baseline=want_cpu)
