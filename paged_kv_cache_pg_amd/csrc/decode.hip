@@ -494,9 +494,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
 
-// Ring depth: bf16 rows keep three steps in flight a wave (one more step or one fewer was slower on
-// every batch shape measured); float32 rows, twice the registers a step, keep one.  The depth
-// changes only when loads are issued, never the arithmetic, so results do not depend on it.
+// Ring depth: bf16 rows keep three steps in flight a wave.  One step was slower wherever CUs sat idle
+// (1 to 3 streams of 40960 keys) and no faster when all were busy; seven was slower for workgroups
+// of 2 and 4 heads and spills with 8.  float32 rows, twice the registers a step, keep one.  The
+// depth changes only when loads are issued, never the arithmetic, so results do not depend on it.
 // Launches the split kernel over streams a.s0 .. a.s0 + n - 1.
 template <int ET, int G>
 hipError_t launch_split_t(const DecArgs& a, int n, hipStream_t st) {
