@@ -441,56 +441,56 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
 }
 
 // Merge a (stream, head)'s split partials in split order; thread d owns dimension d.
-static_assert(MAX_SPLITS <= 64, "the combine kernel keeps one split a lane of its first wave");
+static_assert(MAX_SPLITS <= 64, "the combine kernel keeps one split a lane");
 
-// A stream's output rows are its nq window queries x hq heads (one query in plain decode).
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// A stream's output rows are its nq window queries x hq heads (one query in plain decode).  Every wave
+// derives the splits' weights itself (lane c holds split c's (m, l); the reference max and the
+// running sum walk the lanes in split order through scalar reads), so no wave waits on another.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
-  __shared__ float s_scale[MAX_SPLITS];
-  __shared__ float s_L;
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int64_t rows = (int64_t)a.hq * a.nq;
   const int64_t row0 = ((int64_t)s * rows + h) * a.ns_max;
   // Every load is issued before any result is needed: the split count (from the stream's length),
-  // the splits' (m, l) and this thread's output dimension of every split slot.  Slots past the
-  // stream's split count hold stale values and are never used.
+  // the splits' (m, l) and this thread's output dimension of every split slot (slots past ns_max
+  // read the last slot; slots past the stream's split count are never used).
   const int n = stream_keys(a, s);
   float po[MAX_SPLITS];
 #pragma unroll
-  for (int c = 0; c < MAX_SPLITS; ++c) po[c] = c < a.ns_max ? a.part_o[(row0 + c) * HD + d] : 0.f;
+  for (int c = 0; c < MAX_SPLITS; ++c) po[c] = a.part_o[(row0 + min(c, a.ns_max - 1)) * HD + d];
   const int lc = threadIdx.x & 63;
-  float mc = NEG_INF, lv = 0.f;
-  if (threadIdx.x < 64 && lc < a.ns_max) {
-    mc = a.part_ml[(row0 + lc) * 2];
-    lv = a.part_ml[(row0 + lc) * 2 + 1];
-  }
+  const int64_t mrow = row0 + min(lc, a.ns_max - 1);
+  float mc = a.part_ml[mrow * 2], lv = a.part_ml[mrow * 2 + 1];
   const int ns = dec_splits(n);
   float* outp = a.out + ((int64_t)s * rows + h) * HD;
   if (ns == 0) {
     outp[d] = 0.f;
     return;
   }
-  if (threadIdx.x < 64) {
-    if (lc >= ns) {
-      mc = NEG_INF;
-      lv = 0.f;
-    }
-    float M = mc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float sc = (mc == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    if (lc < MAX_SPLITS) s_scale[lc] = sc;
-    // L in split order (lane 0 walks the splits)
-    const float term = sc * lv;
-    float L = 0.f;
-    for (int cc = 0; cc < ns; ++cc) L += __shfl(term, cc);
-    if (lc == 0) s_L = L;
+  if (lc >= ns) {
+    mc = NEG_INF;
+    lv = 0.f;
   }
-  __syncthreads();
-  float O = 0.f;
+  float M = NEG_INF;
+#pragma unroll
+  for (int cc = 0; cc < MAX_SPLITS; ++cc) M = fmaxf(M, lane_f(mc, cc));
+  const float sc = (mc == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+  // The partials were loaded before (m, l), so they have landed by now; taking them here keeps the
+  // compiler from moving each load under its split's test below (one memory round trip a split).
+#pragma unroll
+  for (int c = 0; c < MAX_SPLITS; ++c) asm volatile("" : "+v"(po[c]));
+  // L and O in split order
+  const float term = sc * lv;
+  float L = 0.f, O = 0.f;
 #pragma unroll
   for (int c = 0; c < MAX_SPLITS; ++c)
-    if (c < ns) O += s_scale[c] * po[c];
-  const float L = s_L;
+    if (c < ns) {
+      L += lane_f(term, c);
+      O += lane_f(sc, c) * po[c];
+    }
   outp[d] = (L > 0.f) ? O / L : 0.f;
 }
 

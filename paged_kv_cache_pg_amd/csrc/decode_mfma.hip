@@ -44,6 +44,11 @@ constexpr float RESCALE_SLACK = 8.f;     // log2 units a row's reference max may
 
 static_assert(VBUF >= 16 * HD * 4, "a wave's partial O must fit in its staging buffer");
 
+// The row a masked key reads in place of its own (and the word read in place of a block id or a table
+// entry when there are none): zero bytes, whose e4m3 codes are zeros, so a masked key's V row adds
+// 0 x 0 to the PV product with no select, whatever the arena holds.  Never written.
+__device__ __attribute__((aligned(16))) char zero_row[2 * HD];
+
 // 8 e4m3 codes (two dwords) widened to 8 bf16, exactly.
 __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -99,20 +104,28 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
   // Key ids: key (tile tt, lane) is position i = (t_begin + tt) * 64 + lane (dense) or 4 * ids[i / 4] + i % 4
   // (sparse); -1 when masked.  Every index is clamped so each load reads valid memory.
+  // The loads take no branch around them (one under a branch makes the compiler drain every load
+  // in flight before the next use of any of them): with no ids or no table they read a word of the
+  // zero row, and the value read always enters the result (as + 0), so no path can drop the load.
+  // The zero row's address is taken once, kept in scalar registers.
+  const char __attribute__((address_space(1)))* zg = (const char __attribute__((address_space(1)))*)zero_row;
+  asm volatile("" : "+s"(zg));
+  const char* zrow = (const char*)zg;
   auto load_id = [&](int tt) -> int {
-    if (a.ids == nullptr) return 0;
     const int i = (t_begin + tt) * TILE + l;
-    return a.ids[(int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0)];
+    const int* p = a.ids != nullptr ? a.ids + ((int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0))
+                                    : (const int*)zrow;
+    return *p;
   };
+  auto load_entry = [&](int pos) -> int32_t { return *pg_entry(a.pg, s, pos >= 0 ? pos : 0, (const int32_t*)zrow); };
+  auto entry_page = [&](int32_t e) -> int32_t { return e + (a.pg.table != nullptr ? 0 : s); };
   auto key_pos = [&](int tt, int id) -> int {
     const int i = (t_begin + tt) * TILE + l;
     if (i >= n || tt >= T) return -1;
-    if (a.ids == nullptr) return i;
+    if (a.ids == nullptr) return i + id;  // id: the zero word
     return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
   };
 
-  // The stream's first q row: valid memory of 512 bytes, read in place of masked keys.
-  const char* dummy = (const char*)a.q + (int64_t)s * W * a.hq * (2 * HD);
 
   // Q^T fragments (B operand): lane holds row c16's dims 32ds + 8u .. +7 (bf16 K), or for e4m3 K, step
   // ds = 2t + h, dims 64t + 16u + 8h .. +7 (the dims the widened codes of a 16-byte load hold).
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
   // Load slot i of a tile: i < NK is K block kb = i % 4, step i / 4 (16 keys x 64 bytes); then the two
   // halves' V loads, each 2 (bf16) or 4 (e4m3) rows of 512 / 256 contiguous bytes.
-  auto load_slot = [&](int tt, int i, uint4& x, bool& ok) {
+  auto load_slot = [&](int tt, int i, uint4& x) {
     const bool ok_t = tt < T;
     int key;
     int boff;
@@ -146,8 +159,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
       base = a.vb;
     }
     const int64_t off = s_keyat[w][tt & 1][key];
-    ok = ok_t && off >= 0;
-    const char* p = (ok ? base + off : dummy) + boff;
+    const char* p = (ok_t && off >= 0 ? base + off : zrow) + boff;
     x = i < NK ? ld_k(p) : ld_stream(p);
   };
 
@@ -160,10 +172,14 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
   // region's first scale and gets V scale 0.
   auto scale_off = [&](int32_t page, int pos) -> int64_t { return pos >= 0 ? pg_offset(a.pg, page, gk, pos, 4) : 0; };
 
+  // Bit k of the ballot of a tile: key k of the tile has a row (key_at >= 0).
+  uint64_t kv_cur = 0;
+
   if (T > 0) {
     {
       const int pos0 = key_pos(0, load_id(0));
-      const int32_t page0 = pg_page(a.pg, s, pos0 >= 0 ? pos0 : 0);
+      const int32_t page0 = entry_page(load_entry(pos0));
+      kv_cur = __ballot(pos0 >= 0);
       s_keyat[w][0][l] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
       if constexpr (FP8) {
         const int64_t so = scale_off(page0, pos0);
@@ -175,14 +191,18 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
     int id_next = load_id(1);
     wave_lds_sync();
     uint4 rx[R];
-    bool rok[R];
 #pragma unroll
-    for (int d = 0; d < R; ++d) load_slot(0, d, rx[d], rok[d]);
+    for (int d = 0; d < R; ++d) load_slot(0, d, rx[d]);
 
+    // key_ids -> key_at for tile t+1: the table entry is read at the top of tile t, the row offsets
+    // written at slot IKA (the entry has long landed, so waiting for it drains no load in flight) and
+    // first read at slot NS - R, by the prefetch of tile t+1's first slot
+    constexpr int IKA = NS - R - 4;
+    static_assert(IKA >= 4, "the table entry needs a few slots to land");
     for (int t = 0; t < T; ++t) {
-      // key_ids -> key_at for tile t+1, written at slot 4 and first read R slots before tile t+1
       const int pos1 = key_pos(t + 1, id_next);
-      const int32_t page1 = pg_page(a.pg, s, pos1 >= 0 ? pos1 : 0);
+      const int32_t e1 = load_entry(pos1);
+      const uint64_t kv_next = __ballot(pos1 >= 0);
       id_next = load_id(t + 2);
       float ks1 = 0.f, vs1 = 0.f;
 
@@ -193,7 +213,8 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
       static_for<NS>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        if constexpr (i == 4) {
+        if constexpr (i == IKA) {
+          const int32_t page1 = entry_page(e1);
           s_keyat[w][(t + 1) & 1][l] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
           if constexpr (FP8) {
             const int64_t so = scale_off(page1, pos1);
@@ -203,10 +224,9 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
           wave_lds_sync();
         }
         const uint4 x = rx[i % R];
-        const bool ok = rok[i % R];
         // prefetch slot i + R (possibly of the next tile)
-        if constexpr (i + R < NS) load_slot(t, i + R, rx[i % R], rok[i % R]);
-        else load_slot(t + 1, i + R - NS, rx[i % R], rok[i % R]);
+        if constexpr (i + R < NS) load_slot(t, i + R, rx[i % R]);
+        else load_slot(t + 1, i + R - NS, rx[i % R]);
 
         if constexpr (i < NK) {
           // ---- S^T += K Q^T: key block kb, one (bf16) or two (e4m3) 32-dim steps ----
@@ -221,8 +241,8 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
         if constexpr (i == NK - 1) {
           // ---- online softmax over tile t: lane holds keys 16kb + 4u + e of its row ----
-          const int64_t* ka = s_keyat[w][t & 1];
           const int kbase = (t_begin + t) * TILE;
+          const uint64_t kvl = kv_cur >> (4 * u);  // bit 16kb + e: the lane's key 16kb + 4u + e has a row
           float z[4][4];
           float mx = NEG_INF;
 #pragma unroll
@@ -234,8 +254,9 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int key = 16 * kb + 4 * u + e;
-              const bool valid = vrow && (a.ids == nullptr ? kbase + key < lim : ka[key] >= 0);
+              // a key counts when it has a row and, for a window's query, is not past the query
+              bool valid = vrow & (((kvl >> (16 * kb + e)) & 1) != 0);
+              if constexpr (W > 1) valid = valid & (kbase + 16 * kb + 4 * u + e < lim);
               z[kb][e] = valid ? sacc[kb][e] * (a.zscale * ksc[e]) : NEG_INF;
               mx = fmaxf(mx, z[kb][e]);
             }
@@ -286,7 +307,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
         if constexpr (FP8) {
           // tile t+1's scales, stored once their loads have long landed (read from tile t+1 on)
-          if constexpr (i == NK) {
+          if constexpr (i == NS - 1) {
             s_ks[w][(t + 1) & 1][l] = ks1;
             s_vs[w][(t + 1) & 1][l] = pos1 >= 0 ? vs1 : 0.f;
           }
@@ -297,11 +318,10 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
           constexpr int j = (i - NK) % NVH, hf = (i - NK) / NVH;
           char* vbuf = s_v[w];
           if constexpr (FP8) {
-            // masked keys read stand-in bytes that may hold NaN codes: they become zeros
+            // a masked key's row is the zero row: zero codes
             const int row = 4 * j + (l >> 4), cc = l & 15;
-            const uint4 y = ok ? x : make_uint4(0u, 0u, 0u, 0u);
-            *(bf16x8*)(vbuf + row * VROWB + v_slot(row, 2 * cc) * 16) = widen8(y.x, y.y);
-            *(bf16x8*)(vbuf + row * VROWB + v_slot(row, 2 * cc + 1) * 16) = widen8(y.z, y.w);
+            *(bf16x8*)(vbuf + row * VROWB + v_slot(row, 2 * cc) * 16) = widen8(x.x, x.y);
+            *(bf16x8*)(vbuf + row * VROWB + v_slot(row, 2 * cc + 1) * 16) = widen8(x.z, x.w);
           } else {
             const int row = 2 * j + (l >> 5), cc = l & 31;
             *(uint4*)(vbuf + row * VROWB + v_slot(row, cc) * 16) = x;
@@ -330,6 +350,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
           }
         }
       });
+      kv_cur = kv_next;
     }
   }
 
