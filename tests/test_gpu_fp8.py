@@ -224,6 +224,65 @@ def test_fp8_sparse_matches_oracle_and_all_blocks_equal_dense():
     assert np.array_equal(sp.view(np.uint32), dn.view(np.uint32))
 
 
+def _poisoned(lens, hkv, ptok, KC, VC, KS, VS, rng, unlisted=None):
+    """An arena over whole pages whose bytes outside the valid rows are e4m3 NaN codes (0xFF) and
+    NaN scales: each stream's positions from its length to the end of its last page, and the rows of
+    the blocks in unlisted[s] (ids of 4-row blocks)."""
+    S = len(lens)
+    pages = [max(1, (L + ptok - 1) // ptok) for L in lens]
+    cap = max(pages) * ptok
+    KCf = np.full((S, hkv, cap, D), 0xFF, np.uint8)
+    VCf = np.full((S, hkv, cap, D), 0xFF, np.uint8)
+    KSf = np.full((S, hkv, cap), np.nan, np.float32)
+    VSf = np.full((S, hkv, cap), np.nan, np.float32)
+    for s, L in enumerate(lens):
+        KCf[s, :, :L], VCf[s, :, :L] = KC[s, :, :L], VC[s, :, :L]
+        KSf[s, :, :L], VSf[s, :, :L] = KS[s, :, :L], VS[s, :, :L]
+        for b in (unlisted[s] if unlisted is not None else []):
+            KCf[s, :, 4 * b:4 * b + 4] = 0xFF
+            VCf[s, :, 4 * b:4 * b + 4] = 0xFF
+            KSf[s, :, 4 * b:4 * b + 4] = np.nan
+            VSf[s, :, 4 * b:4 * b + 4] = np.nan
+    table, n_pages = make_table("shuffled", pages, rng)
+    pl = PlacedFp8([p * ptok for p in pages], hkv, ptok, KCf, VCf, KSf, VSf, table=table, n_pages=n_pages)
+    pl.lens_list = [int(L) for L in lens]   # attend over the valid rows only
+    pl.lens = dev(np.array(lens, np.int32))
+    return pl
+
+
+def test_fp8_masked_keys_read_no_arena_bytes():
+    """Masked keys (past a stream's end inside its last tile and page, invalid block ids, the empty
+    slots of a block list) read a row of zeros in place of their own: with every arena byte outside
+    the attended rows an e4m3 NaN code and every such scale NaN, decode and sparse attention stay
+    finite and within the bar of the oracle over the valid rows."""
+    lens = [1000, 77, 513]
+    hq, hkv, ptok = 16, 2, 64
+    rng, q, KC, VC, KS, VS = _draw(71, lens, hkv, hq)
+    qd = dev(q)
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    Kd, Vd = O.e4m3_dequantize(KC, KS), O.e4m3_dequantize(VC, VS)
+    pl = _poisoned(lens, hkv, ptok, KC, VC, KS, VS, rng)
+    got = decode_fp8(pl, qd, hq, 1 / 16).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert rel_err_rows(got, _oracle_decode(q, KC, VC, KS, VS, lens, 1 / 16)) <= TOL
+    # sparse: the rows of every block not listed are NaN too
+    k = 64
+    nblk = [L // 4 for L in lens]
+    sel = [np.sort(rng.choice(n, min(n, 40), replace=False)) for n in nblk]
+    unlisted = [sorted(set(range(n)) - set(x.tolist())) for n, x in zip(nblk, sel)]
+    pl = _poisoned(lens, hkv, ptok, KC, VC, KS, VS, rng, unlisted)
+    ids = np.full((len(lens), k), -1, np.int32)
+    for s in range(len(lens)):
+        ids[s, :len(sel[s])] = sel[s]
+    ids[2, 40] = 99999                      # an id past the blocks: masked
+    cnt = np.array([len(x) for x in sel], np.int32)
+    cnt[2] += 1
+    got = _sparse(pl, qd, hq, ids, cnt, k, max(lens))
+    assert np.all(np.isfinite(got))
+    ref = O.sparse(qf, Kd, Vd, [list(x) for x in sel], 1 / 16)
+    assert rel_err_rows(got, ref) <= TOL
+
+
 def _store(lens_before, n_new, hkv, ptok, rows_k, rows_v, table, n_pages, max_len):
     """Append n_new bf16 rows a stream at positions lens_before[s] into a zero e4m3 arena."""
     S = len(lens_before)
