@@ -126,7 +126,6 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
     return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
   };
 
-
   // Q^T fragments (B operand): lane holds row c16's dims 32ds + 8u .. +7 (bf16 K), or for e4m3 K, step
   // ds = 2t + h, dims 64t + 16u + 8h .. +7 (the dims the widened codes of a 16-byte load hold).
   bf16x8 qf[8];
