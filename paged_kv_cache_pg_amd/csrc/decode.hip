@@ -562,8 +562,9 @@ hipError_t launch_split_g(const DecArgs& a0, int G, int n, bool short_keys, hipS
 
 // A batch whose grid takes more than one round of workgroups (one a CU) and ends in a partial round
 // runs as two split launches: the streams of the whole rounds, then the rest, whose smaller grid
-// the head split above can spread over all CUs (5 streams at 40960 keys: 4 + 1).  Every stream's
-// output is the same either way; one combine merges them all.
+// the head split above can spread over all CUs.  A rest of one stream takes one more with it (5
+// streams at 40960 keys: 3 + 2, 9: 7 + 2), as one stream alone keeps too few bytes in flight.
+// Every stream's output is the same either way; one combine merges them all.
 template <int ET>
 hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
   const int max_keys = a.ids != nullptr ? 4 * a.ids_stride : a.max_len;
@@ -573,6 +574,7 @@ hipError_t launch_g(const DecArgs& a, int G, int n_streams, hipStream_t st) {
   if (!short_keys && w > 0 && w <= cus) {
     const int per_round = (int)(cus / w);
     if (n_streams > per_round && n_streams % per_round != 0) first = n_streams - n_streams % per_round;
+    if (n_streams - first == 1 && per_round >= 2) first -= 1;
   }
   hipError_t e = launch_split_g<ET>(a, G, first, short_keys, st);
   if (e == hipSuccess && first < n_streams) {

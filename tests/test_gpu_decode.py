@@ -87,8 +87,8 @@ def test_mixed_pair_concurrent_equals_solo():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_batch_split_in_two_launches_equals_each_stream_alone(dtype):
     """5 streams of 8192+ keys over 4 KV heads make 5 x 64 workgroups of 8 heads, one round (256 CUs)
-    and a quarter: the first 4 streams run as one launch and the fifth as a second launch whose heads
-    are spread over 4 workgroups each (float32 rows: groups of 8 always run as two workgroups of 4).
+    and a quarter: the first 3 streams run as one launch and the last 2 as a second launch whose heads
+    are spread over 2 workgroups each (float32 rows: groups of 8 always run as two workgroups of 4).
     Every stream's output equals the stream decoded alone (itself a launch with the heads spread),
     bit for bit, and the oracle within 2e-3."""
     lens = [8200, 9000, 8192, 12000, 8500]
