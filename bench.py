@@ -38,10 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
 DECODE_TRAFFIC_BYTES = 676_366_084
-DECODE_TRAFFIC_SOURCES = "0ba23debf66966e3"
+DECODE_TRAFFIC_SOURCES = "9133c6ade51b8598"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 345_923_897
-FP8_TRAFFIC_SOURCES = "3470f9a00f130187"
+FP8_TRAFFIC_BYTES = 345_922_822
+FP8_TRAFFIC_SOURCES = "ed2c947c92c2e60c"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")
