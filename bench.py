@@ -40,8 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_TRAFFIC_BYTES = 676_366_084
 DECODE_TRAFFIC_SOURCES = "9133c6ade51b8598"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 345_922_822
-FP8_TRAFFIC_SOURCES = "ed2c947c92c2e60c"
+FP8_TRAFFIC_BYTES = 345_969_913
+FP8_TRAFFIC_SOURCES = "a9633d4b21050321"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")

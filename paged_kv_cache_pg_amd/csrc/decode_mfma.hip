@@ -69,7 +69,11 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
   static_assert(ROWS <= 16, "the window's query rows must fit one MFMA column block");
   static_assert(NS % R == 0 && R < NS - 8, "ring slots must be compile-time and the tile long enough");
 
-  __shared__ int64_t s_keyat[NWAVE][2][TILE];
+  // key_at of a tile kept as the K and V row pointers themselves (the zero row for a masked key), so a
+  // load adds only its byte offset: no select, no base, no sign test a load
+  typedef const char __attribute__((address_space(1)))* gptr;
+  __shared__ gptr s_kp[NWAVE][2][TILE];
+  __shared__ gptr s_vp[NWAVE][2][TILE];
   __shared__ __attribute__((aligned(16))) float s_ks[FP8 ? NWAVE : 1][2][TILE];
   __shared__ __attribute__((aligned(16))) float s_vs[FP8 ? NWAVE : 1][2][TILE];
   __shared__ __attribute__((aligned(16))) char s_v[NWAVE][VBUF];
@@ -142,24 +146,20 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
   // Load slot i of a tile: i < NK is K block kb = i % 4, step i / 4 (16 keys x 64 bytes); then the two
   // halves' V loads, each 2 (bf16) or 4 (e4m3) rows of 512 / 256 contiguous bytes.
+  // (The key_at of a tile past the wave's last holds the zero row for every key.)
   auto load_slot = [&](int tt, int i, uint4& x) {
-    const bool ok_t = tt < T;
     int key;
     int boff;
-    const char* base;
     if (i < NK) {
       key = 16 * (i & 3) + c16;
       boff = 64 * (i >> 2) + 16 * u;
-      base = a.kb;
     } else {
       const int j = (i - NK) % NVH, hf = (i - NK) / NVH;
       key = FP8 ? HALF * hf + 4 * j + (l >> 4) : HALF * hf + 2 * j + (l >> 5);
       boff = FP8 ? 16 * (l & 15) : 16 * (l & 31);
-      base = a.vb;
     }
-    const int64_t off = s_keyat[w][tt & 1][key];
-    const char* p = (ok_t && off >= 0 ? base + off : zrow) + boff;
-    x = i < NK ? ld_k(p) : ld_stream(p);
+    const gptr p = (i < NK ? s_kp : s_vp)[w][tt & 1][key] + boff;
+    x = i < NK ? ld_k((const char*)p) : ld_stream((const char*)p);
   };
 
   f32x4 oacc[16];
@@ -179,7 +179,11 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
       const int pos0 = key_pos(0, load_id(0));
       const int32_t page0 = entry_page(load_entry(pos0));
       kv_cur = __ballot(pos0 >= 0);
-      s_keyat[w][0][l] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
+      {
+        const int64_t off = pg_offset(a.pg, page0, gk, pos0 >= 0 ? pos0 : 0, ROWB);
+        s_kp[w][0][l] = pos0 >= 0 ? (gptr)(a.kb + off) : zg;
+        s_vp[w][0][l] = pos0 >= 0 ? (gptr)(a.vb + off) : zg;
+      }
       if constexpr (FP8) {
         const int64_t so = scale_off(page0, pos0);
         const float ks = *(const float*)(a.ksb + so), vs = *(const float*)(a.vsb + so);
@@ -214,7 +218,11 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
         constexpr int i = decltype(I)::value;
         if constexpr (i == IKA) {
           const int32_t page1 = entry_page(e1);
-          s_keyat[w][(t + 1) & 1][l] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
+          {
+            const int64_t off = pg_offset(a.pg, page1, gk, pos1 >= 0 ? pos1 : 0, ROWB);
+            s_kp[w][(t + 1) & 1][l] = pos1 >= 0 ? (gptr)(a.kb + off) : zg;
+            s_vp[w][(t + 1) & 1][l] = pos1 >= 0 ? (gptr)(a.vb + off) : zg;
+          }
           if constexpr (FP8) {
             const int64_t so = scale_off(page1, pos1);
             ks1 = *(const float*)(a.ksb + so);
