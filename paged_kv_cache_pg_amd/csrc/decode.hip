@@ -31,6 +31,12 @@ namespace paged {
 
 namespace {
 
+// 1 KiB of zero bytes (a float32 row): the row a masked key reads (its zero V adds 0 to the PV sums,
+// and its score is replaced by -inf), and the word read in place of a block id or a table entry when
+// there are none (its value then adds nothing).  Never written.
+__device__ __attribute__((aligned(16))) char zero_row_d[1024];
+typedef const char __attribute__((address_space(1)))* gptr_t;
+
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PAGED_DEC_RING
 #define PAGED_DEC_RING 4         // 4-key steps of bf16 K/V buffered a lane (float32 rows: 2)
@@ -195,7 +201,10 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
   static_assert(SPT % RING == 0, "ring slots must be compile-time");
   using Buf = StepBuf<ET>;
 
-  __shared__ int64_t s_keyat[NWAVE][4][TILE];
+  // key_at kept as the K and V row pointers themselves (the zero row for a masked key), so a load adds
+  // only its byte offset: no select, no base, no sign test a load
+  __shared__ gptr_t s_kp[NWAVE][4][TILE];
+  __shared__ gptr_t s_vp[NWAVE][4][TILE];
   __shared__ float s_sc[NWAVE][TILE * G];
   __shared__ float s_alpha[NWAVE][G];
   __shared__ float s_o[NWAVE][G][HD];
@@ -227,48 +236,50 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
   const int j32 = lane & 31, half = lane >> 5;
   const int max_blocks = a.max_len >> 2;
 
-  // q row of this (stream, KV head): always-valid memory of one row, read in place of masked keys.
+  // q rows of this (stream, KV head)
   const char* qrow = (const char*)a.q + ((int64_t)s * a.hq + (int64_t)g * G) * QROWB;
+  // The zero row (its address taken once, kept in scalar registers): the row a masked key reads, and
+  // the word read in place of a block id or a table entry when there are none.
+  gptr_t zg = (gptr_t)zero_row_d;
+  asm volatile("" : "+s"(zg));
+  const char* zrow = (const char*)zg;
 
   // Key ids: key (tile tt, lane) is position i = (t_begin + tt) * 64 + lane (dense) or 4 * ids[i / 4] + i % 4
   // (sparse); -1 when masked.  The id and table loads are issued early and finished later so that their
   // latency hides behind the steps in flight; every index is clamped so each load reads valid memory.
-  // Both are issued whether or not there is an id list or a table (reading the q row instead): a load
-  // under a branch leaves the compiler unsure how many loads follow it, and its wait for that load
-  // becomes a wait for every load in flight.
+  // Both are issued whether or not there is an id list or a table (reading a word of the zero row
+  // instead, which then enters the result as + 0, so that no path can drop the load): a load under a
+  // branch leaves the compiler unsure how many loads follow it, and its wait for that load becomes a
+  // wait for every load in flight.
   auto load_id = [&](int tt) -> int {
     const int i = (t_begin + tt) * TILE + lane;
     const int32_t* p = a.ids != nullptr ? a.ids + ((int64_t)s * a.ids_stride + ((i < n && tt < T) ? (i >> 2) : 0))
-                                        : (const int32_t*)qrow;
-    const int v = *p;
-    return a.ids != nullptr ? v : 0;
+                                        : (const int32_t*)zrow;
+    return *p;  // the zero word when there are no ids
   };
   auto load_page = [&](int pos) -> int32_t {
-    const int32_t e = *pg_entry(a.pg, s, pos >= 0 ? pos : 0, (const int32_t*)qrow);
-    return a.pg.table != nullptr ? e : s;
+    const int32_t e = *pg_entry(a.pg, s, pos >= 0 ? pos : 0, (const int32_t*)zrow);
+    return e + (a.pg.table != nullptr ? 0 : s);  // e: the zero word when there is no table
   };
   auto key_pos = [&](int tt, int id) -> int {
     const int i = (t_begin + tt) * TILE + lane;
     if (i >= n || tt >= T) return -1;
-    if (a.ids == nullptr) return i;
+    if (a.ids == nullptr) return i + id;  // id: the zero word
     return (id >= 0 && id < max_blocks) ? 4 * id + (i & 3) : -1;
   };
 
   // Loads of global step gs = SPT * tt + i: i < NSTEP is K step i of tile tt, else V step i - NSTEP.
-  // Every load is issued (masked keys and steps past the wave's tiles read the q row instead) so none
-  // sits under a branch.
+  // Every load is issued (masked keys, and every key of a tile past the wave's last, read the zero row
+  // instead) so none sits under a branch.
   auto load_step = [&](int tt, int i, Buf& b) {
-    const bool ok_t = tt < T;
     if (i < NSTEP) {
-      const int64_t off = s_keyat[w][tt & 3][4 * i + grp];
-      const char* kp = (ok_t && off >= 0) ? a.kb + off : qrow;
+      const char* kp = (const char*)s_kp[w][tt & 3][4 * i + grp];
 #pragma unroll
       for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream(kp + 256 * cc + 16 * jj);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t off = s_keyat[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
-        const char* vp = (ok_t && off >= 0) ? a.vb + off : qrow;
+        const char* vp = (const char*)s_vp[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
 #pragma unroll
         for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream(vp + 512 * cc + 16 * j32);
       }
@@ -294,7 +305,9 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
     {
       const int pos0 = key_pos(0, load_id(0));
       const int32_t page0 = load_page(pos0);
-      s_keyat[w][0][lane] = pos0 >= 0 ? pg_offset(a.pg, page0, gk, pos0, ROWB) : (int64_t)-1;
+      const int64_t off0 = pg_offset(a.pg, page0, gk, pos0 >= 0 ? pos0 : 0, ROWB);
+      s_kp[w][0][lane] = pos0 >= 0 ? (gptr_t)(a.kb + off0) : zg;
+      s_vp[w][0][lane] = pos0 >= 0 ? (gptr_t)(a.vb + off0) : zg;
     }
     int id_next = load_id(1);
     wave_lds_sync();
@@ -312,7 +325,9 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
         if (i == 4) {
-          s_keyat[w][(t + 1) & 3][lane] = pos1 >= 0 ? pg_offset(a.pg, page1, gk, pos1, ROWB) : (int64_t)-1;
+          const int64_t off1 = pg_offset(a.pg, page1, gk, pos1 >= 0 ? pos1 : 0, ROWB);
+          s_kp[w][(t + 1) & 3][lane] = pos1 >= 0 ? (gptr_t)(a.kb + off1) : zg;
+          s_vp[w][(t + 1) & 3][lane] = pos1 >= 0 ? (gptr_t)(a.vb + off1) : zg;
           wave_lds_sync();
         }
         if (i == NSTEP) {
@@ -368,7 +383,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
           R::run(acc, res);
           const int kk = 4 * i + grp;
           if ((lane & 3) == 0 && R::writer_row(row)) {
-            const bool valid = s_keyat[w][t & 3][kk] >= 0;
+            const bool valid = s_kp[w][t & 3][kk] != zg;
 #pragma unroll
             for (int k = 0; k < R::NR; ++k)
               s_sc[w][kk * G + R::head(row, k)] = valid ? res[k] * a.zscale : NEG_INF;
