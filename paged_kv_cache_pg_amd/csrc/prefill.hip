@@ -79,7 +79,11 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
   __shared__ __attribute__((aligned(16))) char s_k1[TILEB];
   __shared__ __attribute__((aligned(16))) char s_v0[TILEB];
   __shared__ __attribute__((aligned(16))) char s_v1[TILEB];
-  __shared__ int64_t s_keyat[2][PF_KT];
+  // key_at of a tile kept as the K and V row pointers themselves (the first q row for a key past the
+  // keys, valid and finite memory), so a load adds only its chunk offset
+  typedef const char __attribute__((address_space(1)))* gptr;
+  __shared__ gptr s_kp[2][PF_KT];
+  __shared__ gptr s_vp[2][PF_KT];
 
   // w is read from the first lane so that the compiler knows it is the same across the wave (wave-uniform
   // LDS addresses, such as the destinations of the global->LDS loads, then stay in scalar registers)
@@ -128,22 +132,22 @@ __global__ __launch_bounds__(PF_THREADS, PAGED_PF_WG_PER_CU) void prefill_kernel
   auto stage_keyat = [&](int tt, int32_t page) {
     if (tid < PF_KT && tt < nt) {
       const int key = tt * PF_KT + tid;
-      s_keyat[tt & 1][tid] = key < kmax ? pg_offset(a.pg, page, g, key, ROWB) : (int64_t)-1;
+      const int64_t off = pg_offset(a.pg, page, g, key < kmax ? key : 0, ROWB);
+      s_kp[tt & 1][tid] = key < kmax ? (gptr)(a.kb + off) : (gptr)a.q;
+      s_vp[tt & 1][tid] = key < kmax ? (gptr)(a.vb + off) : (gptr)a.q;
     }
   };
   // One tile's K and V rows, global -> LDS directly (no registers): load i of wave w fills LDS
   // slots (8w + i) * 64 + lane, i.e. rows 2(8w + i) and 2(8w + i) + 1 of each buffer, each lane
   // fetching the chunk that belongs in its slot (the slot maps are involutions).  Keys past kmax
-  // read the first q row instead (valid, finite memory): masked keys then meet a zero weight.
-  const char* dummy = (const char*)a.q;
+  // read the first q row instead (their key_at): masked keys then meet a zero weight.
   auto load_tile = [&](int tt, char* kbuf, char* vbuf) {
 #pragma unroll
     for (int i = 0; i < LD_PER_WAVE; ++i) {
       const int slot = (LD_PER_WAVE * w + i) * 64 + l;
       const int row = slot / CH, pos = slot % CH;
-      const int64_t off = s_keyat[tt & 1][row];
-      const char* ks = (off >= 0 ? a.kb + off : dummy) + k_slot(row, pos) * 16;
-      const char* vs = (off >= 0 ? a.vb + off : dummy) + v_slot(row, pos) * 16;
+      const char* ks = (const char*)s_kp[tt & 1][row] + k_slot(row, pos) * 16;
+      const char* vs = (const char*)s_vp[tt & 1][row] + v_slot(row, pos) * 16;
       __builtin_amdgcn_global_load_lds((const void*)ks,
                                        (__attribute__((address_space(3))) void*)(kbuf + (LD_PER_WAVE * w + i) * 1024),
                                        16, 0, 0);
