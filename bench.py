@@ -37,11 +37,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_358_100
-DECODE_TRAFFIC_SOURCES = "18a014ed41d90dc5"
+DECODE_TRAFFIC_BYTES = 676_350_935
+DECODE_TRAFFIC_SOURCES = "2f6f09b83dc8ec71"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 345_965_515
-FP8_TRAFFIC_SOURCES = "e0f78c871ff98b99"
+FP8_TRAFFIC_BYTES = 346_138_061
+FP8_TRAFFIC_SOURCES = "d45ec72f67be5431"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")

@@ -34,7 +34,8 @@ namespace {
 
 // A K fragment load takes 64 bytes of each of 16 rows; the other half of each 128-byte line is read
 // a few loads later, so K loads are ordinary cached loads (marked nontemporal, the lines left before
-// their second half was read and K was fetched from HBM twice).  V loads read whole lines: streamed.
+// their second half was read and K was fetched from HBM twice).  V loads read whole lines: streamed
+// (ld_stream, nontemporal unless four workgroups of a KV head read the same rows).
 __device__ __forceinline__ uint4 ld_k(const char* p) { return *(const uint4*)p; }
 
 constexpr int HALF = 32;                 // keys a PV half tile
@@ -58,7 +59,7 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int ET, int G, int W, int R>
+template <int ET, int G, int W, int R, bool NT>
 __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
   constexpr bool FP8 = ET == ET_FP8;
   constexpr int NK = FP8 ? 16 : 32;      // K loads a tile (4 key blocks x 4 or 8 steps)
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
       boff = FP8 ? 16 * (l & 15) : 16 * (l & 31);
     }
     const gptr p = (i < NK ? s_kp : s_vp)[w][tt & 1][key] + boff;
-    x = i < NK ? ld_k((const char*)p) : ld_stream((const char*)p);
+    x = i < NK ? ld_k((const char*)p) : ld_stream<NT>((const char*)p);
   };
 
   f32x4 oacc[16];
@@ -397,7 +398,10 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 template <int ET, int G, int W>
 hipError_t launch_w(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
-  hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING>), grid, dim3(WGS), 0, st, a);
+  if (dec_nontemporal(a.kvshift))
+    hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING, true>), grid, dim3(WGS), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING, false>), grid, dim3(WGS), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(a, n_streams, st);

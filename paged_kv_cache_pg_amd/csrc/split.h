@@ -17,9 +17,6 @@
 #ifndef PAGED_DEC_NWAVE
 #define PAGED_DEC_NWAVE 8        // waves a workgroup (a split is shared by its waves)
 #endif
-#ifndef PAGED_DEC_NT
-#define PAGED_DEC_NT 1           // streamed K/V loads marked nontemporal
-#endif
 
 namespace paged {
 
@@ -53,15 +50,22 @@ __device__ __forceinline__ int stream_keys(const DecArgs& a, int s) {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte load of streamed K/V data (read once: no reuse to keep in cache).
+// 16-byte load of streamed K/V data.  NT marks it nontemporal (rows read once, nothing to keep in
+// cache); the hint changes where lines are kept, never a loaded value.
+template <bool NT>
 __device__ __forceinline__ uint4 ld_stream(const char* p) {
-#if PAGED_DEC_NT
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-#else
-  const u32x4_t v = *(const u32x4_t*)p;
-#endif
+  u32x4_t v;
+  if constexpr (NT) v = __builtin_nontemporal_load((const u32x4_t*)p);
+  else v = *(const u32x4_t*)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// Whether a launch's K/V loads are nontemporal.  Where the q heads of a KV head are spread over four
+// workgroups (2^kvshift), which read the same rows, plain loads leave the lines in L2 for the other
+// three: sparse attention over 3 x 2048 keys 15.1 -> 13.3 us, one stream of 40960 keys 55.5 -> 53.5
+// us.  With one or two workgroups a head the nontemporal hint is faster (4 x 40960: 112.5 against
+// 128.1 us with plain loads; 2 x 40960: 71.8 against 76.9).
+__host__ __device__ inline bool dec_nontemporal(int kvshift) { return kvshift < 2; }
 
 // Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
 __device__ __forceinline__ void wave_lds_sync() {
