@@ -37,11 +37,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per decode launch (split + combine) from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled
 # by the same counters on a copy of known size (profiles/decode_4x40960_p256_hbm_traffic.md); valid
 # only for the kernel sources that were measured.
-DECODE_TRAFFIC_BYTES = 676_350_935
-DECODE_TRAFFIC_SOURCES = "2f6f09b83dc8ec71"
+DECODE_TRAFFIC_BYTES = 676_356_870
+DECODE_TRAFFIC_SOURCES = "9be177aa5ee9f53a"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 346_138_061
-FP8_TRAFFIC_SOURCES = "d45ec72f67be5431"
+FP8_TRAFFIC_BYTES = 346_130_480
+FP8_TRAFFIC_SOURCES = "b05e89fdf98b260d"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")

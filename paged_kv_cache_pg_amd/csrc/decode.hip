@@ -186,7 +186,7 @@ struct StepBuf {
   uint4 x[Rows<ET>::NCQ];
 };
 
-template <int ET, int G, int RING, bool NT>
+template <int ET, int G, int RING, bool NTK, bool NTV>
 __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
   using RT = Rows<ET>;
   constexpr int ROWB = RT::ROWB;     // bytes a K/V row
@@ -275,13 +275,13 @@ __global__ __launch_bounds__(WGS, 1) void decode_split_kernel(DecArgs a) {
     if (i < NSTEP) {
       const char* kp = (const char*)s_kp[w][tt & 3][4 * i + grp];
 #pragma unroll
-      for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream<NT>(kp + 256 * cc + 16 * jj);
+      for (int cc = 0; cc < NCQ; ++cc) b.x[cc] = ld_stream<NTK>(kp + 256 * cc + 16 * jj);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const char* vp = (const char*)s_vp[w][tt & 3][4 * (i - NSTEP) + 2 * j + half];
 #pragma unroll
-        for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream<NT>(vp + 512 * cc + 16 * j32);
+        for (int cc = 0; cc < NCP; ++cc) b.x[NCP * j + cc] = ld_stream<NTV>(vp + 512 * cc + 16 * j32);
       }
     }
   };
@@ -518,8 +518,12 @@ template <int ET, int G>
 hipError_t launch_split_t(const DecArgs& a, int n, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv << a.kvshift, n);
   constexpr int R = ET == ET_BF16 ? PAGED_DEC_RING : 2;
-  if (dec_nontemporal(a.kvshift)) hipLaunchKernelGGL((decode_split_kernel<ET, G, R, true>), grid, dim3(WGS), 0, st, a);
-  else hipLaunchKernelGGL((decode_split_kernel<ET, G, R, false>), grid, dim3(WGS), 0, st, a);
+  if (dec_v_nontemporal(a.kvshift))
+    hipLaunchKernelGGL((decode_split_kernel<ET, G, R, true, true>), grid, dim3(WGS), 0, st, a);
+  else if (dec_k_nontemporal(a.kvshift))
+    hipLaunchKernelGGL((decode_split_kernel<ET, G, R, true, false>), grid, dim3(WGS), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<ET, G, R, false, false>), grid, dim3(WGS), 0, st, a);
   return hipGetLastError();
 }
 

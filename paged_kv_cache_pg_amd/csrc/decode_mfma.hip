@@ -35,7 +35,7 @@ namespace {
 // A K fragment load takes 64 bytes of each of 16 rows; the other half of each 128-byte line is read
 // a few loads later, so K loads are ordinary cached loads (marked nontemporal, the lines left before
 // their second half was read and K was fetched from HBM twice).  V loads read whole lines: streamed
-// (ld_stream, nontemporal unless four workgroups of a KV head read the same rows).
+// (ld_stream, nontemporal unless several workgroups of a KV head read the same rows).
 __device__ __forceinline__ uint4 ld_k(const char* p) { return *(const uint4*)p; }
 
 constexpr int HALF = 32;                 // keys a PV half tile
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 template <int ET, int G, int W>
 hipError_t launch_w(const DecArgs& a, int n_streams, hipStream_t st) {
   dim3 grid(a.ns_max, a.hkv << a.kvshift, n_streams);
-  if (dec_nontemporal(a.kvshift))
+  if (dec_v_nontemporal(a.kvshift))
     hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING, true>), grid, dim3(WGS), 0, st, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<ET, G, W, PAGED_DECM_RING, false>), grid, dim3(WGS), 0, st, a);

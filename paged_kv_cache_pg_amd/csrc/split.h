@@ -60,12 +60,14 @@ __device__ __forceinline__ uint4 ld_stream(const char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Whether a launch's K/V loads are nontemporal.  Where the q heads of a KV head are spread over four
-// workgroups (2^kvshift), which read the same rows, plain loads leave the lines in L2 for the other
-// three: sparse attention over 3 x 2048 keys 15.1 -> 13.3 us, one stream of 40960 keys 55.5 -> 53.5
-// us.  With one or two workgroups a head the nontemporal hint is faster (4 x 40960: 112.5 against
-// 128.1 us with plain loads; 2 x 40960: 71.8 against 76.9).
-__host__ __device__ inline bool dec_nontemporal(int kvshift) { return kvshift < 2; }
+// Whether a launch's K and V loads are nontemporal, by the number of workgroups (2^kvshift) over which
+// the q heads of a KV head are spread; those workgroups read the same rows.  One workgroup a head:
+// both nontemporal (4 x 40960: 112.5 us, against 128.1 with plain loads).  Two: V loads plain, so that
+// the V lines stay in L2 for the other workgroup (2 x 40960 72.4-73.1 -> 68.9-70.0 us, 5 x 40960
+// about 160 -> 154-156; plain K loads as well were slower, 76.9).  Four: both plain (sparse attention
+// over 3 x 2048 keys 15.1 -> 13.1-13.3 us, 1 x 40960 55.9 -> 53.6; plain V only, 13.5-13.7).
+__host__ __device__ inline bool dec_k_nontemporal(int kvshift) { return kvshift < 2; }
+__host__ __device__ inline bool dec_v_nontemporal(int kvshift) { return kvshift < 1; }
 
 // Orders this wave's LDS writes before its later LDS reads (no cross-wave sync).
 __device__ __forceinline__ void wave_lds_sync() {
