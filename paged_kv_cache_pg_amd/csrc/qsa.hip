@@ -71,6 +71,28 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 // lane's blocks are requested together, then the rows; the queries are summed while the rows are in
 // flight.
 // ---------------------------------------------------------------------------
+// Cross-lane steps with DPP (row shifts, row broadcasts, quad and half-row permutations): the value
+// moves between lanes inside the vector unit, with no LDS round trip as a shuffle takes.  Called with
+// every lane of the wave active.  A lane whose source is outside its row, or whose row is masked off,
+// takes `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWS, 0xf, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror: lane i of each 8 takes lane 7 - i
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;  // row_shr:n
+constexpr int DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143;  // row_bcast:15 / :31
+
+// A float64 moved by a DPP pattern whose sources are all inside the row (quad and half-row ones).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = dpp_u32<CTRL, 0xf>((uint32_t)u, 0u), hi = dpp_u32<CTRL, 0xf>((uint32_t)(u >> 32), 0u);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SC_THREADS = 256;
@@ -169,9 +191,11 @@ __global__ __launch_bounds__(SC_THREADS) void scores_kernel(TopkArgs a) {
           if (4 * c + e < a.idx_dim) acc = acc + (double)p[e] * q[e];
       }
     }
-    acc = acc + __shfl_xor(acc, 1);
-    acc = acc + __shfl_xor(acc, 2);
-    acc = acc + __shfl_xor(acc, 4);
+    // the butterfly: after the quad steps every lane of a quad holds its quad's sum, so the half-row
+    // mirror adds the other quad's
+    acc = acc + dpp_f64<DPP_QUAD_XOR1>(acc);
+    acc = acc + dpp_f64<DPP_QUAD_XOR2>(acc);
+    acc = acc + dpp_f64<DPP_HALF_MIRROR>(acc);
     const int b = b_wave + 8 * r + slot;
     if (j == 0 && b < nb) a.scores[(int64_t)s * a.max_blocks + b] = acc;
   }
@@ -252,6 +276,64 @@ __device__ __forceinline__ void lds_count(uint32_t* hist, uint32_t bin) {
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+
+// Inclusive prefix sum over the wave's 64 lanes in lane order (sums within rows of 16 by row shifts,
+// then the last lane of row 0 added to row 1 and of row 2 to row 3, then lane 31 to rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp_u32<DPP_SHR1, 0xf>(x, 0u);
+  x += dpp_u32<DPP_SHR2, 0xf>(x, 0u);
+  x += dpp_u32<DPP_SHR4, 0xf>(x, 0u);
+  x += dpp_u32<DPP_SHR8, 0xf>(x, 0u);
+  x += dpp_u32<DPP_BCAST15, 0xa>(x, 0u);
+  x += dpp_u32<DPP_BCAST31, 0xc>(x, 0u);
+  return x;
+}
+
+// Minimum and maximum of a 64-bit value over the wave, in lane 63 (the same steps as the sum; min and
+// max do not depend on the order in which values meet).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x, uint64_t old) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)x, (uint32_t)old);
+  const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(x >> 32), (uint32_t)(old >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void wave_minmax_u64(uint64_t& mn, uint64_t& mx) {
+#define MINMAX_STEP(C, R)                         \
+  {                                               \
+    const uint64_t a = dpp_u64<C, R>(mn, ~0ull);  \
+    const uint64_t b = dpp_u64<C, R>(mx, 0ull);   \
+    mn = a < mn ? a : mn;                         \
+    mx = b > mx ? b : mx;                         \
+  }
+  MINMAX_STEP(DPP_SHR1, 0xf)
+  MINMAX_STEP(DPP_SHR2, 0xf)
+  MINMAX_STEP(DPP_SHR4, 0xf)
+  MINMAX_STEP(DPP_SHR8, 0xf)
+  MINMAX_STEP(DPP_BCAST15, 0xa)
+  MINMAX_STEP(DPP_BCAST31, 0xc)
+#undef MINMAX_STEP
+}
+
+// Exclusive scan of one 32-bit value a thread over the workgroup, in thread order; every thread gets
+// the total.  s_tmp holds TK_WAVES + 1 words.
+__device__ __forceinline__ uint32_t wg_scan32(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_sum(v);
+  if (lane == 63) s_tmp[w] = x;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const uint32_t t = lane < TK_WAVES ? s_tmp[lane] : 0u;
+    const uint32_t z = wave_incl_sum(t);
+    if (lane < TK_WAVES) s_tmp[lane] = z - t;
+    if (lane == TK_WAVES - 1) s_tmp[TK_WAVES] = z;
+  }
+  __syncthreads();
+  const uint32_t r = s_tmp[w] + x - v;
+  *total = s_tmp[TK_WAVES];
+  __syncthreads();
+  return r;
 }
 
 // Exclusive scan of one 64-bit value a thread, in thread order; every thread gets the total.
@@ -346,13 +428,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(TopkArgs a) {
       c[r] = gh[top - r];
       loc += c[r];
     }
-    // exclusive scan over the workgroup, in thread (= descending bin) order
-    uint64_t x = loc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
+    // exclusive scan over the workgroup, in thread (= descending bin) order (counts below 2^28)
+    const uint64_t x = wave_incl_sum((uint32_t)loc);
     if (lane == 63) s_tmp[w] = x;
     __syncthreads();
     uint64_t before = x - loc;
@@ -397,7 +474,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(TopkArgs a) {
       atomicAdd(&s_nt, (uint32_t)__popcll(tm));
       if (cm) cbase = atomicAdd(&s_nc, (uint32_t)__popcll(cm));
     }
-    cbase = __shfl(cbase, 0);
+    cbase = (uint32_t)__builtin_amdgcn_readlane((int)cbase, 0);
     if (cand) {
       const uint32_t slot = cbase + lanes_below(cm);
       keys[slot] = order_key(x[r]);
@@ -500,15 +577,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
         st += v.x;
         sc += v.y;
       }
-      uint32_t it = st, ic = sc;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(it, off), z = __shfl_up(ic, off);
-        if (lane >= off) {
-          it += y;
-          ic += z;
-        }
-      }
+      const uint32_t it = wave_incl_sum(st), ic = wave_incl_sum(sc);
       uint32_t pt = it - st, pc = ic - sc;
       bool over = false;
 #pragma unroll
@@ -569,13 +638,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t y0 = __shfl_xor(kmn, off), y1 = __shfl_xor(kmx, off);
-        kmn = y0 < kmn ? y0 : kmn;
-        kmx = y1 > kmx ? y1 : kmx;
-      }
-      if (lane == 0 && kmx != 0) {
+      wave_minmax_u64(kmn, kmx);
+      if (lane == 63 && kmx != 0) {
         atomicMin((unsigned long long*)&s_kmin, (unsigned long long)kmn);
         atomicMax((unsigned long long*)&s_kmax, (unsigned long long)kmx);
       }
@@ -594,12 +658,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
           c4[r] = s_h2[255 - 4 * lane - r];
           loc += c4[r];
         }
-        uint32_t incl = loc;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
+        const uint32_t incl = wave_incl_sum(loc);
         uint32_t above = incl - loc;
         if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
 #pragma unroll
@@ -648,23 +707,23 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
             r += (int)((ko > kc) | ((ko == kc) & (io < ic)));
           }
         }
-        r += __shfl_xor(r, 1);
-        r += __shfl_xor(r, 2);
+        r += (int)dpp_u32<DPP_QUAD_XOR1, 0xf>((uint32_t)r, 0u);
+        r += (int)dpp_u32<DPP_QUAD_XOR2, 0xf>((uint32_t)r, 0u);
         if (c < n2 && q == 0 && r < k2) select(ic);
       }
       __syncthreads();
       // the ids in id order: thread t's chunks (taken word or'ed with selected word), their counts
       // scanned over the workgroup in thread (= id) order, then each thread writes its chunks' ids
       uint64_t mk[TK_CPT];
-      uint64_t mine = 0;
+      uint32_t mine = 0;
 #pragma unroll
       for (int j = 0; j < TK_CPT; ++j) {
         const int ch = tid * cpt + j;
         mk[j] = (j < cpt && ch < nchunk) ? (tw[j] | s_sbit[ch]) : 0ull;
-        mine += (uint64_t)__popcll(mk[j]);
+        mine += (uint32_t)__popcll(mk[j]);
       }
-      uint64_t total;
-      uint32_t pos = (uint32_t)wg_scan64(mine, s_tmp, &total);
+      uint32_t total;
+      uint32_t pos = wg_scan32(mine, (uint32_t*)s_tmp, &total);
 #pragma unroll
       for (int j = 0; j < TK_CPT; ++j) {
         uint64_t m = mk[j];
