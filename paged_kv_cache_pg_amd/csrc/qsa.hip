@@ -242,10 +242,10 @@ constexpr int TK_BATCH = 16;        // score chunks a thread reads at once
 #endif
 constexpr int HK_ITEMS = PAGED_HK_ITEMS;  // scores a histogram workgroup
 constexpr int SEL_ITEMS = 1024;     // blocks a selection workgroup
-constexpr int SEL_THREADS = 256;
+constexpr int SEL_THREADS = 1024;  // a thread a block (256: scores + top-k 0.5-1 us slower)
 constexpr int TK_SBITS = 1 << 18;   // blocks a stream whose selected candidates are marked in LDS
 constexpr int TK_CPT = TK_SBITS / 64 / 1024;  // 64-block chunks a thread at most in the id output (4)
-constexpr int HK_THREADS = 256;
+constexpr int HK_THREADS = 1024;   // a thread a score; the bins cleared and flushed 4 a thread (256: 2 us slower)
 
 __device__ __forceinline__ uint64_t order_key(double x) {
   uint64_t u = (uint64_t)__double_as_longlong(x);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(TopkArgs a) {
     s_nt = 0;
     s_nc = 0;
   }
-  // the bin of the k-th block: thread t owns bins 4095 - 16t .. 4080 - 16t (descending)
+  // the bin of the k-th block: thread t owns bins 4095 - BPT t .. 4096 - BPT (t + 1) (descending)
   {
     constexpr int BPT = TK_BINS / SEL_THREADS;
     const uint32_t* gh = a.hist + (int64_t)s * TK_BINS;
