@@ -40,8 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_TRAFFIC_BYTES = 676_356_870
 DECODE_TRAFFIC_SOURCES = "9be177aa5ee9f53a"
 # The same for the e4m3 decode (MFMA kernel + combine; profiles/decode_e4m3_4x40960_p256.md).
-FP8_TRAFFIC_BYTES = 346_130_480
-FP8_TRAFFIC_SOURCES = "b05e89fdf98b260d"
+FP8_TRAFFIC_BYTES = 345_900_367
+FP8_TRAFFIC_SOURCES = "69f3b43ab22f404b"
 
 _DECODE_SOURCES = ("paged_kv_cache_pg_amd/csrc/decode.hip", "paged_kv_cache_pg_amd/csrc/split.h",
                    "paged_kv_cache_pg_amd/csrc/common.h")

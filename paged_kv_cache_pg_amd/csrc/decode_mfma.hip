@@ -33,9 +33,11 @@ namespace {
 #endif
 
 // A K fragment load takes 64 bytes of each of 16 rows; the other half of each 128-byte line is read
-// a few loads later, so K loads are ordinary cached loads (marked nontemporal, the lines left before
-// their second half was read and K was fetched from HBM twice).  V loads read whole lines: streamed
-// (ld_stream, nontemporal unless several workgroups of a KV head read the same rows).
+// by the next load, and K loads are ordinary cached loads (marked nontemporal when the halves were four
+// loads apart, the lines left before their second half was read and K was fetched from HBM twice; with
+// the halves back to back, nontemporal K measured no faster for e4m3 and slower for the bf16 window).
+// V loads read whole lines: streamed (ld_stream, nontemporal unless several workgroups of a KV head
+// read the same rows).
 __device__ __forceinline__ uint4 ld_k(const char* p) { return *(const uint4*)p; }
 
 constexpr int HALF = 32;                 // keys a PV half tile
@@ -145,15 +147,17 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
     }
   }
 
-  // Load slot i of a tile: i < NK is K block kb = i % 4, step i / 4 (16 keys x 64 bytes); then the two
-  // halves' V loads, each 2 (bf16) or 4 (e4m3) rows of 512 / 256 contiguous bytes.
+  // Load slot i of a tile: i < NK is K block kb = (i / 2) % 4, step st = 2 (i / 8) + i % 2 (16 keys x 64
+  // bytes), so that slots i and i + 1 read the two halves of the same 128-byte lines (e4m3 step 63.0-63.4
+  // -> 61.7-62.2 us against blocks in the inner place); each block still takes its steps in increasing
+  // order.  Then the two halves' V loads, each 2 (bf16) or 4 (e4m3) rows of 512 / 256 contiguous bytes.
   // (The key_at of a tile past the wave's last holds the zero row for every key.)
   auto load_slot = [&](int tt, int i, uint4& x) {
     int key;
     int boff;
     if (i < NK) {
-      key = 16 * (i & 3) + c16;
-      boff = 64 * (i >> 2) + 16 * u;
+      key = 16 * ((i >> 1) & 3) + c16;
+      boff = 64 * (((i >> 3) << 1) | (i & 1)) + 16 * u;
     } else {
       const int j = (i - NK) % NVH, hf = (i - NK) / NVH;
       key = FP8 ? HALF * hf + 4 * j + (l >> 4) : HALF * hf + 2 * j + (l >> 5);
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(WGS, 1) void decode_mfma_kernel(DecArgs a) {
 
         if constexpr (i < NK) {
           // ---- S^T += K Q^T: key block kb, one (bf16) or two (e4m3) 32-dim steps ----
-          constexpr int kb = i & 3, st = i >> 2;
+          constexpr int kb = (i >> 1) & 3, st = ((i >> 3) << 1) | (i & 1);
           if constexpr (FP8) {
             sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(x.x, x.y), qf[2 * st], sacc[kb], 0, 0, 0);
             sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(x.z, x.w), qf[2 * st + 1], sacc[kb], 0, 0, 0);
