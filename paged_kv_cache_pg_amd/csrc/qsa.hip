@@ -57,20 +57,6 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Scores.  In exact arithmetic sum_h sum_d qI[h][d] p[d] = sum_d q[d] p[d] with q[d] = sum_h qI[h][d],
-// so the workgroup first sums the indexer queries over the heads (float64, head by head) into LDS.
-// A block is then scored by 8 lanes: lane j of the block takes the 4-dim chunks c = j, j+8, j+16, ...
-// of its pooled row (so the 8 lanes of a block read 128 contiguous bytes a load), adds each product
-// p[d] * q[d] (rounded to float64, not fused) to its float64 sum in increasing dim order, and the 8
-// lane sums meet in a fixed butterfly, ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)) (float64 addition
-// commutes, so every lane of the block ends with the same value).  This is the order of the oracle's
-// definition, so scores are bit for bit the oracle's.
-// A wave scores 8 blocks a round and R rounds (2 for 128-wide rows), all of whose row loads are issued
-// before the first sum; a workgroup is 4 waves.  The stream's length and the table entries of a
-// lane's blocks are requested together, then the rows; the queries are summed while the rows are in
-// flight.
-// ---------------------------------------------------------------------------
 // Cross-lane steps with DPP (row shifts, row broadcasts, quad and half-row permutations): the value
 // moves between lanes inside the vector unit, with no LDS round trip as a shuffle takes.  Called with
 // every lane of the wave active.  A lane whose source is outside its row, or whose row is masked off,
@@ -93,6 +79,20 @@ __device__ __forceinline__ double dpp_f64(double x) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// ---------------------------------------------------------------------------
+// Scores.  In exact arithmetic sum_h sum_d qI[h][d] p[d] = sum_d q[d] p[d] with q[d] = sum_h qI[h][d],
+// so the workgroup first sums the indexer queries over the heads (float64, head by head) into LDS.
+// A block is then scored by 8 lanes: lane j of the block takes the 4-dim chunks c = j, j+8, j+16, ...
+// of its pooled row (so the 8 lanes of a block read 128 contiguous bytes a load), adds each product
+// p[d] * q[d] (rounded to float64, not fused) to its float64 sum in increasing dim order, and the 8
+// lane sums meet in a fixed butterfly, ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)) (float64 addition
+// commutes, so every lane of the block ends with the same value).  This is the order of the oracle's
+// definition, so scores are bit for bit the oracle's.
+// A wave scores 8 blocks a round and R rounds (2 for 128-wide rows), all of whose row loads are issued
+// before the first sum; a workgroup is 4 waves.  The stream's length and the table entries of a
+// lane's blocks are requested together, then the rows; the queries are summed while the rows are in
+// flight.
+// ---------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SC_THREADS = 256;
@@ -277,7 +277,6 @@ __device__ __forceinline__ void lds_count(uint32_t* hist, uint32_t bin) {
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
-
 
 // Inclusive prefix sum over the wave's 64 lanes in lane order (sums within rows of 16 by row shifts,
 // then the last lane of row 0 added to row 1 and of row 2 to row 3, then lane 31 to rows 2 and 3).
