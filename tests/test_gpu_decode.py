@@ -89,8 +89,9 @@ def test_batch_split_in_two_launches_equals_each_stream_alone(dtype):
     """5 streams of 8192+ keys over 4 KV heads make 5 x 64 workgroups of 8 heads, one round (256 CUs)
     and a quarter: the first 3 streams run as one launch and the last 2 as a second launch whose heads
     are spread over 2 workgroups each (float32 rows: groups of 8 always run as two workgroups of 4).
-    Every stream's output equals the stream decoded alone (itself a launch with the heads spread),
-    bit for bit, and the oracle within 2e-3."""
+    Every stream's output equals the stream decoded alone (itself a launch with the heads spread over
+    4 workgroups), bit for bit, and the oracle within 2e-3.  The three launches also take the three
+    load-hint choices (K and V nontemporal; V plain; both plain), which must not change a value."""
     lens = [8200, 9000, 8192, 12000, 8500]
     w = make_workload(12, lens, 256, 32, 4, dtype=dtype, table_kind="shuffled")
     pl = Placed(w, paged=True)
